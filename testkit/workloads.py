@@ -1,0 +1,85 @@
+"""The synthetic attention workloads: shapes, scales, masking and seeds.
+
+Shapes follow the pages' problem statement (Learning FlashAttention the Hard
+Way, Part 2, workload definitions: SDPA_L = [1,4,128,64] for listings and
+SDPA_P = [1,8,4096,64] for timing, fp16 Q/K/V in [B,H,S,D] from randn, default
+scale 1/sqrt(D)), widened with a long-sequence case, two causal cases at
+head_dim 128, and one with Q and K drawn three times wider so the softmax is
+peaked and the running max moves often.
+
+Q, K and V use generator streams 0, 1 and 2 under the workload's seed.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .gen import normal_f16
+
+STREAM_Q, STREAM_K, STREAM_V = 0, 1, 2
+SEED_BASE = 0xA77E0000
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    causal: bool
+    seed: int
+    qk_mult: float = 1.0  # Q and K are fp16(qk_mult * N(0,1))
+    v_mult: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(D), rounded to fp32 (both sides use this value)."""
+        return float(np.float32(1.0 / np.sqrt(self.D)))
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.S, self.D)
+
+    @property
+    def flops(self) -> float:
+        """4*B*H*S^2*D, halved when causal (the pages' FLOP convention)."""
+        f = 4.0 * self.B * self.H * self.S * self.S * self.D
+        return f / 2 if self.causal else f
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V and O in fp16 plus LSE in fp32, each moved once."""
+        n = self.B * self.H * self.S * self.D
+        return 4 * n * 2 + self.B * self.H * self.S * 4
+
+    def describe(self) -> str:
+        m = "causal" if self.causal else "non-causal"
+        return f"B{self.B} H{self.H} S{self.S} D{self.D} fp16 {m}"
+
+
+WORKLOADS = {
+    "listing_b1h4s128d64": Workload("listing_b1h4s128d64", 1, 4, 128, 64, False, SEED_BASE + 1),
+    "sdpa_b1h8s4096d64": Workload("sdpa_b1h8s4096d64", 1, 8, 4096, 64, False, SEED_BASE + 2),
+    "long_b1h8s16384d64": Workload("long_b1h8s16384d64", 1, 8, 16384, 64, False, SEED_BASE + 3),
+    "causal_b2h16s8192d128": Workload("causal_b2h16s8192d128", 2, 16, 8192, 128, True, SEED_BASE + 4),
+    "peaked_causal_b4h32s4096d128": Workload(
+        "peaked_causal_b4h32s4096d128", 4, 32, 4096, 128, True, SEED_BASE + 5, qk_mult=3.0),
+}
+
+HEADLINE = "sdpa_b1h8s4096d64"
+
+
+def make_qkv(B: int, H: int, S: int, D: int, seed: int,
+             qk_mult: float = 1.0, v_mult: float = 1.0):
+    """fp16 numpy Q, K, V of shape [B,H,S,D] from streams 0, 1, 2 of ``seed``."""
+    shape = (B, H, S, D)
+    q = normal_f16(seed, STREAM_Q, shape, qk_mult)
+    k = normal_f16(seed, STREAM_K, shape, qk_mult)
+    v = normal_f16(seed, STREAM_V, shape, v_mult)
+    return q, k, v
+
+
+def workload_inputs(w: Workload):
+    return make_qkv(w.B, w.H, w.S, w.D, w.seed, w.qk_mult, w.v_mult)
