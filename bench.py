@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step is one attn_fwd launch over the whole workload (inputs resident in
+device memory). Prints ONE JSON line with throughput (TFLOP/s), the kernel's
+roofline position against the dense fp16 MFMA peak, and the CPU oracle timed
+on the host as a baseline (which also checks the GPU answer).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+# Published MI355X dense peaks / bandwidth (no sparsity).
+PEAK_FP16_MFMA_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "attn fwd TFLOP/s & µs, fp16 B1 H8 S4096 D64; % of dense FP16 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (for profiler runs)")
+    ap.add_argument("--cpu-sample-rows", type=int, default=0,
+                    help="rows per head for the CPU leg (0 = every row)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, sample_rows: int):
+    """Time the fp64 oracle on the host over a bounded sample of the workload and
+    compare the GPU output with it on that sample."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                            if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas_threads = 1
+    S = w.S
+    if sample_rows and sample_rows < S:
+        rows = np.linspace(0, S - 1, sample_rows).round().astype(np.int64)
+        desc = f"{sample_rows} evenly spaced query rows of each of the {w.B * w.H} heads"
+    else:
+        rows = None
+        desc = f"the whole workload: all {w.B * w.H} heads x {S} query rows"
+    t0 = time.perf_counter()
+    if rows is None:
+        O, L = oracle.sdpa_forward(q, k, v, w.scale, w.causal)
+        n_rows = w.B * w.H * S
+    else:
+        O = np.empty((w.B, w.H, len(rows), w.D))
+        L = np.empty((w.B, w.H, len(rows)))
+        for b in range(w.B):
+            for h in range(w.H):
+                O[b, h], L[b, h] = oracle.sdpa_rows(q, k, v, w.scale, w.causal, b, h, rows)
+        n_rows = w.B * w.H * len(rows)
+    secs = time.perf_counter() - t0
+    # FLOPs of the sample under the same convention as the GPU figure
+    flops = w.flops * n_rows / (w.B * w.H * S)
+    og = o_gpu if rows is None else o_gpu[:, :, rows]
+    lg = lse_gpu if rows is None else lse_gpu[:, :, rows]
+    err = np.abs(og.astype(np.float64) - O)
+    parity = {"o_max_abs": float(err.max()), "o_mean_abs": float(err.mean()),
+              "lse_max_abs": float(np.abs(lg.astype(np.float64) - L).max()),
+              "pass": bool(err.max() <= 4e-3 and err.mean() <= 5e-4
+                           and np.abs(lg.astype(np.float64) - L).max() <= 1e-3)}
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": blas_threads,
+            "kind": "oracle", "sample": desc, "seconds": secs,
+            "note": "fp64 numpy oracle; matmuls on BLAS threads, exp/max/sum single-threaded"}, parity
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py is single-GPU; launch it without torch.distributed", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_forward_05_amd as attn
+    from testkit import HEADLINE, WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+    log(f"workload {w.name}: {w.describe()}")
+    q, k, v = workload_inputs(w)
+    qt, kt, vt = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    o = torch.empty_like(qt)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        attn.fwd(qt, kt, vt, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    log(f"warmup {args.warmup} done")
+
+    # Per-launch device time from events recorded on the launch stream.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    durs_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    avg_ms = float(durs_ms.mean())
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms, kernel avg {avg_ms * 1e3:.2f} us, "
+        f"median {np.median(durs_ms) * 1e3:.2f} us, min {durs_ms.min() * 1e3:.2f} us")
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (avg_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "causal": w.causal, "scale": w.scale, "seed": w.seed,
+                   "qk_mult": w.qk_mult},
+        "us_per_launch": {"mean": round(avg_ms * 1e3, 3),
+                          "median": round(float(np.median(durs_ms)) * 1e3, 3),
+                          "min": round(float(durs_ms.min()) * 1e3, 3)},
+        "pct_of_peak": round(100.0 * achieved / PEAK_FP16_MFMA_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": PEAK_FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": f"attn_fwd_kernel<{w.D},{str(w.causal).lower()}>",
+                     "algorithmic_flops_per_launch": w.flops,
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline:
+        log("CPU oracle leg ...")
+        o_np = o.cpu().numpy()
+        l_np = lse.cpu().numpy()
+        base, parity = cpu_baseline(w, q, k, v, o_np, l_np, args.cpu_sample_rows)
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+        log(f"CPU oracle {base['seconds']:.2f} s, parity {parity}")
+        if not parity["pass"]:
+            log("PARITY FAILED: the GPU result does not match the oracle")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    if result.get("parity") and not result["parity"]["pass"]:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

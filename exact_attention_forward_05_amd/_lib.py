@@ -1,0 +1,64 @@
+"""ctypes binding of the C ABI declared in include/attn_fwd.h.
+
+Argument marshalling only: the library does all of the work on the GPU. If the
+library has not been built, loading raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn_fwd.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+                4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_ARG", 6: "ATTN_ERR_HIP"}
+
+# (name, restype, argtypes) of every exported entry point
+_SIGNATURES = [
+    ("attn_fwd", ctypes.c_int,
+     [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+      ctypes.c_void_p]),
+    ("attn_status_string", ctypes.c_char_p, [ctypes.c_int]),
+    ("attn_last_error", ctypes.c_char_p, []),
+    ("attn_version", ctypes.c_int, []),
+]
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libattn_fwd.so (once). Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -m exact_attention_forward_05_amd.build` "
+                "(the attention path has no CPU fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, res, args in _SIGNATURES:
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, load().attn_last_error().decode(errors="replace"))
+
+
+def attn_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
+             S: int, D: int, scale: float, causal: int, stream: int) -> int:
+    """Raw call of the C entry point with integer addresses; returns the status."""
+    return load().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D,
+                           ctypes.c_float(scale), causal, stream)

@@ -1,0 +1,95 @@
+/*
+ * attn_fwd.h -- C ABI of the fused exact-attention forward library
+ * (libattn_fwd.so, HIP kernels for AMD Instinct MI355X / gfx950).
+ *
+ * Operation (scaled dot-product attention, forward only):
+ *
+ *   O[b,h,i,:] = sum_j softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:]) * V[b,h,j,:]
+ *   LSE[b,h,i] = ln sum_j exp(scale * Q[b,h,i,:] . K[b,h,j,:])
+ *
+ * over the visible keys j: every j < S, or j <= i when causal. This is the
+ * attention of "Learning FlashAttention the Hard Way, Part 2" (workload
+ * definitions: fp16 Q, K, V of shape [B,H,S,D], default scale 1/sqrt(D)),
+ * computed as one streaming kernel that folds K/V tiles into a running
+ * (max, denominator, unnormalised output) carrier held in registers (Part 2,
+ * introduction and Moves 1-4), so that scores never reach device memory.
+ * The causal mask and the LSE output are additions to the pages' problem
+ * statement: key j is hidden from query i when j > i (the diagonal is
+ * visible), and LSE is in natural-log units of the scaled scores.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device. The
+ *    caller allocates and owns every buffer; the library allocates nothing,
+ *    frees nothing, never synchronises and never changes the current device.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*; NULL means the default stream). Buffers must stay valid until
+ *    that work completes. Kernel faults surface at the caller's next
+ *    synchronisation on the stream, not in the return code.
+ *  - Errors are returned as attn_status codes. Argument checks run on the
+ *    host before any HIP call, so an invalid call touches no device state.
+ *    A thread-local message with details is available from attn_last_error().
+ *  - The library keeps no state besides that message and is reentrant.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_FWD_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,         /* a required pointer is NULL                   */
+  ATTN_ERR_SHAPE = 2,        /* B, H or S < 1, or the tensors are too large  */
+  ATTN_ERR_UNSUPPORTED = 3,  /* head dimension D not in {64, 128}            */
+  ATTN_ERR_ALIGN = 4,        /* q/k/v/o not 16-byte or lse not 4-byte aligned*/
+  ATTN_ERR_ARG = 5,          /* causal not 0/1, or scale not finite          */
+  ATTN_ERR_HIP = 6           /* the HIP launch reported an error             */
+} attn_status;
+
+/*
+ * attn_fwd -- fused attention forward.
+ *
+ *  q, k, v : const fp16 (IEEE binary16), contiguous row-major [B, H, S, D];
+ *            element (b,h,s,d) at offset ((b*H + h)*S + s)*D + d.
+ *            Q, K and V share one shape (self-attention, S_q = S_k = S).
+ *  o       : fp16 output, same shape and layout as q. Written with
+ *            round-to-nearest-even from the fp32 result.
+ *  lse     : fp32 output [B, H, S]; element (b,h,s) at (b*H + h)*S + s.
+ *  B, H, S : batch, heads, sequence length; each >= 1, and B*H*S*D < 2^40.
+ *            S need not be a multiple of any tile size.
+ *  D       : head dimension, 64 or 128.
+ *  scale   : softmax scale applied to Q.K (finite; any sign; 0 gives uniform
+ *            weights). Callers wanting the usual default pass 1/sqrt(D).
+ *  causal  : 0 = every key visible, 1 = key j hidden from query i if j > i.
+ *  stream  : hipStream_t as void* (NULL = default stream).
+ *
+ *  o and lse must not alias q, k, v or each other. Non-finite inputs are not
+ *  checked and propagate to the outputs. Products are exact and accumulate
+ *  in fp32; the softmax runs in fp32 in base 2 with the scale folded in; the
+ *  probabilities are rounded to fp16 for the P.V product.
+ *
+ *  Returns ATTN_OK once the kernel is enqueued, or an error code (nothing is
+ *  enqueued on error).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int S, int D, float scale, int causal, void* stream);
+
+/* Static English name of a status code ("ATTN_OK", ...); never NULL. */
+const char* attn_status_string(int status);
+
+/* Thread-local detail of the last error returned on this thread ("" if none).
+ * The pointer stays valid until the next call into the library on this
+ * thread. */
+const char* attn_last_error(void);
+
+/* ATTN_FWD_ABI_VERSION of the loaded library. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,61 @@
+"""Helpers shared by the GPU parity tests: run the HIP path, compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+# Tolerance for fp16 inputs drawn from N(0,1) (and its 3x-scaled variant),
+# against the fp64 oracle over the same fp16 operands: O max abs error, O mean
+# abs error, and LSE max abs error. The GPU rounds P and O to fp16 (RNE);
+# half an fp16 ulp at |O| in [4, 8) is 1.95e-3, within the max bound.
+O_MAX_ABS = 4e-3
+O_MEAN_ABS = 5e-4
+LSE_MAX_ABS = 1e-3
+
+
+def gpu_available() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def run_gpu(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool):
+    """Copy fp16 numpy inputs to cuda:0, run the library, return numpy (o fp16, lse fp32)."""
+    import torch
+
+    import exact_attention_forward_05_amd as attn
+
+    dev = torch.device("cuda:0")
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (q, k, v))
+    o, lse = attn.fwd(qt, kt, vt, scale=scale, causal=causal)
+    torch.cuda.synchronize(dev)
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray,
+            what: str = "", o_max=O_MAX_ABS, o_mean=O_MEAN_ABS, lse_max=LSE_MAX_ABS) -> dict:
+    """Element-wise comparison; raises AssertionError with the worst element."""
+    og = o_gpu.astype(np.float64)
+    lg = lse_gpu.astype(np.float64)
+    assert np.isfinite(og).all(), f"{what}: non-finite O from the GPU"
+    assert np.isfinite(lg).all(), f"{what}: non-finite LSE from the GPU"
+    err = np.abs(og - o_ref)
+    lerr = np.abs(lg - lse_ref)
+    stats = {"o_max": float(err.max()), "o_mean": float(err.mean()),
+             "lse_max": float(lerr.max())}
+    worst = np.unravel_index(int(err.argmax()), err.shape)
+    assert stats["o_max"] <= o_max, f"{what}: O max abs err {stats['o_max']:.3e} at {worst}"
+    assert stats["o_mean"] <= o_mean, f"{what}: O mean abs err {stats['o_mean']:.3e}"
+    wl = np.unravel_index(int(lerr.argmax()), lerr.shape)
+    assert stats["lse_max"] <= lse_max, f"{what}: LSE max abs err {stats['lse_max']:.3e} at {wl}"
+    return stats
+
+
+def sample_rows(S: int, rng: np.random.Generator, n_random: int = 24):
+    """Row indices that cover tile edges, the sequence ends and random rows."""
+    fixed = {0, 1, 15, 16, 31, 32, 63, 64, 127, 128, 129, S // 2, S - 129, S - 128, S - 65,
+             S - 64, S - 2, S - 1}
+    rows = {r for r in fixed if 0 <= r < S}
+    rows |= set(int(x) for x in rng.integers(0, S, size=n_random))
+    return np.array(sorted(rows), dtype=np.int64)

@@ -1,0 +1,184 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small cases are compared element by element over the whole output. The large
+workloads are run exactly as the bench launches them and checked on sampled
+rows that the oracle evaluates one by one, plus properties that hold at any
+size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import compare, gpu_available, run_gpu, sample_rows
+from testkit import WORKLOADS, make_qkv, workload_inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _announce(what):
+    print(f"[gpu-parity] {what}", flush=True)
+
+
+SMALL_CASES = [
+    # B, H, S, D, causal, scale, seed
+    (1, 1, 1, 64, False, 0.125, 1),
+    (1, 1, 1, 128, True, 0.125, 2),
+    (1, 2, 17, 64, False, 0.125, 3),
+    (1, 2, 17, 64, True, 0.125, 4),
+    (3, 1, 64, 64, True, 0.125, 5),
+    (1, 1, 127, 64, False, 0.125, 6),
+    (2, 3, 300, 64, False, 0.125, 7),
+    (2, 3, 300, 64, True, 0.125, 8),
+    (1, 2, 129, 128, False, 0.08838834764831845, 9),
+    (1, 2, 129, 128, True, 0.08838834764831845, 10),
+    (2, 2, 257, 128, False, 0.08838834764831845, 11),
+    (1, 1, 1000, 128, True, 0.08838834764831845, 12),
+    (1, 2, 640, 64, True, -0.2, 13),        # negative scale
+    (1, 2, 333, 128, False, 0.5, 14),       # large scale: peaked rows
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: "B{}H{}S{}D{}{}s{}".format(
+    c[0], c[1], c[2], c[3], "c" if c[4] else "n", c[5]))
+def test_small_shapes_full_compare(case):
+    B, H, S, D, causal, scale, seed = case
+    _announce(f"small {case}")
+    q, k, v = make_qkv(B, H, S, D, 9000 + seed)
+    o, l = run_gpu(q, k, v, scale, causal)
+    O, L = oracle.sdpa_forward(q, k, v, scale, causal)
+    compare(o, l, O, L, f"small {case}")
+
+
+def test_listing_workload_full_compare():
+    w = WORKLOADS["listing_b1h4s128d64"]
+    _announce(w.name)
+    q, k, v = workload_inputs(w)
+    o, l = run_gpu(q, k, v, w.scale, w.causal)
+    O, L = oracle.sdpa_forward(q, k, v, w.scale, w.causal)
+    compare(o, l, O, L, w.name)
+
+
+def test_headline_workload_full_compare():
+    w = WORKLOADS["sdpa_b1h8s4096d64"]
+    _announce(w.name)
+    q, k, v = workload_inputs(w)
+    o, l = run_gpu(q, k, v, w.scale, w.causal)
+    O, L = oracle.sdpa_forward(q, k, v, w.scale, w.causal)
+    stats = compare(o, l, O, L, w.name)
+    _announce(f"{w.name} {stats}")
+
+
+@pytest.mark.parametrize("name", ["long_b1h8s16384d64", "causal_b2h16s8192d128",
+                                  "peaked_causal_b4h32s4096d128"])
+def test_large_workload_sampled_rows(name):
+    w = WORKLOADS[name]
+    _announce(name)
+    q, k, v = workload_inputs(w)
+    o, l = run_gpu(q, k, v, w.scale, w.causal)
+    # properties at full size: finite, |O| bounded by max |V| of the head
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    vmax = np.abs(v.astype(np.float32)).max(axis=(2, 3))
+    assert (np.abs(o.astype(np.float32)).max(axis=(2, 3)) <= vmax + 1e-3).all()
+    rng = np.random.default_rng(w.seed)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)]
+    worst = {}
+    for b, h in heads:
+        rows = sample_rows(w.S, rng)
+        O, L = oracle.sdpa_rows(q, k, v, w.scale, w.causal, b, h, rows)
+        st = compare(o[b, h, rows], l[b, h, rows], O, L, f"{name} b{b} h{h}")
+        worst = {kk: max(worst.get(kk, 0.0), vv) for kk, vv in st.items()}
+    _announce(f"{name} {worst}")
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_gives_mean_of_visible_v(causal):
+    B, H, S, D = 1, 2, 200, 64
+    q, k, v = make_qkv(B, H, S, D, 31)
+    o, l = run_gpu(q, k, v, 0.0, causal)
+    vf = v.astype(np.float64)
+    n = np.arange(1, S + 1) if causal else np.full(S, S)
+    mean = np.cumsum(vf, axis=2) / n[None, None, :, None] if causal else \
+        np.broadcast_to(vf.mean(axis=2, keepdims=True), vf.shape)
+    compare(o, l, mean, np.broadcast_to(np.log(n), l.shape), "zero scale")
+
+
+def test_constant_v_rows():
+    B, H, S, D = 2, 2, 300, 128
+    q, k, v = make_qkv(B, H, S, D, 32)
+    v[:] = v[:, :, :1, :]
+    o, l = run_gpu(q, k, v, 0.08838834764831845, True)
+    ref = np.broadcast_to(v[:, :, :1, :].astype(np.float64), o.shape)
+    assert np.abs(o.astype(np.float64) - ref).max() <= 2e-3
+
+
+def test_causal_row0_and_last_row():
+    B, H, S, D = 1, 3, 260, 64
+    q, k, v = make_qkv(B, H, S, D, 33)
+    oc, lc = run_gpu(q, k, v, 0.125, True)
+    on, ln_ = run_gpu(q, k, v, 0.125, False)
+    assert np.array_equal(oc[:, :, 0], v[:, :, 0])
+    s00 = 0.125 * (q[:, :, 0].astype(np.float64) * k[:, :, 0].astype(np.float64)).sum(-1)
+    assert np.abs(lc[:, :, 0] - s00).max() <= 1e-4
+    assert np.abs(oc[:, :, -1].astype(np.float64) - on[:, :, -1]).max() <= 2e-3
+    assert np.abs(lc[:, :, -1] - ln_[:, :, -1]).max() <= 1e-4
+
+
+# ---------------------------------------------------------------- runtime properties
+
+def test_run_to_run_bitwise_determinism():
+    w = WORKLOADS["sdpa_b1h8s4096d64"]
+    q, k, v = workload_inputs(w)
+    o1, l1 = run_gpu(q, k, v, w.scale, False)
+    o2, l2 = run_gpu(q, k, v, w.scale, False)
+    assert np.array_equal(o1.view(np.uint16), o2.view(np.uint16))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+def test_no_writes_outside_outputs_and_nonzero_stream():
+    """Outputs placed inside larger buffers filled with a canary pattern; the
+    call goes through the raw C entry point on a non-default stream."""
+    import torch
+
+    from exact_attention_forward_05_amd import _lib
+
+    B, H, S, D = 2, 2, 200, 128
+    q, k, v = make_qkv(B, H, S, D, 34)
+    dev = torch.device("cuda:0")
+    qt, kt, vt = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    n = B * H * S * D
+    guard = 4096
+    obuf = torch.full((n + 2 * guard,), -7.0, dtype=torch.float16, device=dev)
+    lbuf = torch.full((B * H * S + 2 * guard,), -7.0, dtype=torch.float32, device=dev)
+    st = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(st):
+        rc = _lib.attn_fwd(qt.data_ptr(), kt.data_ptr(), vt.data_ptr(),
+                           obuf.data_ptr() + 2 * guard, lbuf.data_ptr() + 4 * guard,
+                           B, H, S, D, 0.08838834764831845, 1, st.cuda_stream)
+    _lib.check(rc)
+    st.synchronize()
+    ob = obuf.cpu().numpy()
+    lb = lbuf.cpu().numpy()
+    assert (ob[:guard] == -7.0).all() and (ob[guard + n:] == -7.0).all()
+    assert (lb[:guard] == -7.0).all() and (lb[guard + B * H * S:] == -7.0).all()
+    O, L = oracle.sdpa_forward(q, k, v, 0.08838834764831845, True)
+    compare(ob[guard:guard + n].reshape(B, H, S, D), lb[guard:guard + B * H * S].reshape(B, H, S),
+            O, L, "canary")
+
+
+def test_invalid_arguments_raise_without_launch():
+    import torch
+
+    import exact_attention_forward_05_amd as attn
+
+    dev = torch.device("cuda:0")
+    q = torch.zeros((1, 1, 8, 96), dtype=torch.float16, device=dev)
+    with pytest.raises(attn.AttnError, match="ATTN_ERR_UNSUPPORTED"):
+        attn.fwd(q, q, q)
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.float16, device=dev)
+    with pytest.raises(attn.AttnError, match="ATTN_ERR_ARG"):
+        attn.fwd(q, q, q, scale=math.inf)
