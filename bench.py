@@ -34,6 +34,8 @@ def parse():
                     help="skip the CPU oracle leg (for profiler runs)")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows per head for the CPU leg (0 = every row)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -113,6 +115,18 @@ def main():
 
     def step():
         attn.fwd(qt, kt, vt, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+
+    if args.copy_calibration:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
+        # calibrate the HBM byte counters read for the attention kernel.
+        nbytes = 256 << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        log(f"copy calibration: 3 copies of {nbytes} bytes")
+        del src, dst
 
     for _ in range(args.warmup):
         step()

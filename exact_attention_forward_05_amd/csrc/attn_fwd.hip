@@ -67,6 +67,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   const double elems = (double)B * H * (double)S * D;
   if (elems >= 1099511627776.0 || (int64_t)B * H > 0x7fffffff)
     return fail(ATTN_ERR_SHAPE, "B*H*S*D = %.0f elements exceeds 2^40", elems);
+  if ((int64_t)S * D * 2 > 0x7fffffff)
+    return fail(ATTN_ERR_SHAPE, "one head's tensor (S*D*2 = %lld bytes) exceeds 2^31 - 1 bytes",
+                (long long)S * D * 2);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return fail(ATTN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
   if (!aligned(lse, 4)) return fail(ATTN_ERR_ALIGN, "lse must be 4-byte aligned");

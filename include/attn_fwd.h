@@ -58,7 +58,8 @@ typedef enum {
  *  o       : fp16 output, same shape and layout as q. Written with
  *            round-to-nearest-even from the fp32 result.
  *  lse     : fp32 output [B, H, S]; element (b,h,s) at (b*H + h)*S + s.
- *  B, H, S : batch, heads, sequence length; each >= 1, and B*H*S*D < 2^40.
+ *  B, H, S : batch, heads, sequence length; each >= 1, B*H*S*D < 2^40 and
+ *            one head's tensor fits 32-bit byte offsets (S*D*2 < 2^31).
  *            S need not be a multiple of any tile size.
  *  D       : head dimension, 64 or 128.
  *  scale   : softmax scale applied to Q.K (finite; any sign; 0 gives uniform
