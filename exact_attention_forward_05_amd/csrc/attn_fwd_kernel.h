@@ -72,21 +72,17 @@ constexpr uint32_t BUF_FLAGS = 0x00020000u;  // raw buffer, 32-bit data format
 template <int D>
 struct Geometry {
   static constexpr int K_STRIDE = D + PAD;                 // halves per K row
-  static constexpr int V_STRIDE = BLOCK_N + PAD;           // halves per V^T row
   static constexpr int K_HALVES = BLOCK_N * K_STRIDE;
-  static constexpr int V_HALVES = D * V_STRIDE;
-  static constexpr int TILE_HALVES = K_HALVES + V_HALVES;  // one tile (K + V^T)
-  static constexpr int STAGE_HALVES = 2 * TILE_HALVES;     // even + odd tile
-  static constexpr int LDS_BYTES = 2 * STAGE_HALVES * 2;   // two stages
+  static constexpr int V_HALVES = BLOCK_N * D;             // V rows unpadded, swizzled
+  // two-slot rings of tile pairs for K and for V^T
+  static constexpr int LDS_BYTES = (4 * K_HALVES + 4 * V_HALVES) * 2;
   static constexpr int D_CHUNKS = D / 32;                  // contraction chunks of Q.K
   static constexpr int D_BLOCKS = D / 16;                  // 16-row blocks of O^T
-  // per tile pair: K in 16-byte pieces, V in (8 keys x 2 d) units
-  static constexpr int K_PIECES = 2 * BLOCK_N * (D / 8);
-  static constexpr int V_UNITS = 2 * 8 * (D / 2);
-  static constexpr int K_LOADS = K_PIECES / THREADS;
-  static constexpr int V_LOADS = V_UNITS / THREADS;
+  // per tile pair, K and V each in 16-byte pieces
+  static constexpr int PIECES = 2 * BLOCK_N * (D / 8);
+  static constexpr int LOADS = PIECES / THREADS;
   static_assert(D % 64 == 0, "D must be a multiple of 64");
-  static_assert(K_LOADS * THREADS == K_PIECES && V_LOADS * THREADS == V_UNITS, "tiling");
+  static_assert(LOADS * THREADS == PIECES, "tiling");
   // carrier hand-off area (after the key loop): per odd wave, per lane
   static constexpr int CARRIER_FLOATS = QSUB * (2 + 4 * D_BLOCKS);
   static_assert(QGROUPS * 64 * CARRIER_FLOATS * 4 <= LDS_BYTES, "hand-off fits in LDS");
@@ -125,93 +121,81 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Registers holding one prefetched tile pair on its way to LDS.
+// V tile rows are stored unpadded with their 16-byte chunks permuted:
+// chunk c of key row r sits at chunk c ^ v_swizzle(r). The two-dimensional
+// XOR keeps both the 16-byte row writes and the transposing 8-byte reads of
+// the P.V operand free of LDS bank conflicts.
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+  if (D == 64) return 2 * (((r >> 1) & 1) + 2 * ((r >> 3) & 1));
+  return 2 * ((r & 3) + 4 * ((r >> 3) & 1));
+}
+
+// Registers holding prefetched K or V of one tile pair on their way to LDS.
 template <int D>
 struct PairRegs {
-  u32x4 k[Geometry<D>::K_LOADS];
-  uint32_t v[Geometry<D>::V_LOADS][8];
+  u32x4 x[Geometry<D>::LOADS];
 };
 
-// Thread-constant parts of the K/V copy: byte offsets into a head's K/V for
-// key tile 0, and LDS destinations within a stage.
+// Thread-constant parts of the K/V copy: byte offset of each 16-byte piece
+// relative to the first key of a tile pair (the same for K and V), and its
+// LDS destination relative to a ring slot for K and for V.
 template <int D>
 struct CopyPlan {
-  uint32_t k_goff[Geometry<D>::K_LOADS];
-  int k_lds[Geometry<D>::K_LOADS];
-  uint32_t v_goff[Geometry<D>::V_LOADS];
-  int v_lds[Geometry<D>::V_LOADS];
+  uint32_t goff[Geometry<D>::LOADS];
+  int k_lds[Geometry<D>::LOADS];
+  int v_lds[Geometry<D>::LOADS];
 };
 
 template <int D>
 __device__ __forceinline__ void make_copy_plan(CopyPlan<D>& cp, int tid) {
   using G = Geometry<D>;
 #pragma unroll
-  for (int i = 0; i < G::K_LOADS; ++i) {
+  for (int i = 0; i < G::LOADS; ++i) {
     const int u = tid + THREADS * i;
     const int t = u / (BLOCK_N * (D / 8));          // tile of the pair
     const int w = u % (BLOCK_N * (D / 8));
     const int key = w / (D / 8);
-    const int col = (w % (D / 8)) * 8;
-    cp.k_goff[i] = (uint32_t)(((t * BLOCK_N + key) * D + col) * 2);
-    cp.k_lds[i] = t * G::TILE_HALVES + k_row_of(key) * G::K_STRIDE + col;
-  }
-#pragma unroll
-  for (int i = 0; i < G::V_LOADS; ++i) {
-    const int u = tid + THREADS * i;
-    const int t = u / (8 * (D / 2));
-    const int w = u % (8 * (D / 2));
-    const int kg = w % 8;                            // keys 8*kg .. 8*kg+7
-    const int j = w / 8;
-    // d pairs of 16 consecutive lanes land on distinct LDS bank groups
-    const int dp = (j & ~7) + ((j & 7) >> 1) + 4 * (j & 1);
-    cp.v_goff[i] = (uint32_t)(((t * BLOCK_N + 8 * kg) * D + 2 * dp) * 2);
-    cp.v_lds[i] = t * G::TILE_HALVES + G::K_HALVES + (2 * dp) * G::V_STRIDE + 8 * kg;
+    const int chunk = w % (D / 8);
+    cp.goff[i] = (uint32_t)(((t * BLOCK_N + key) * D + 8 * chunk) * 2);
+    cp.k_lds[i] = t * G::K_HALVES + k_row_of(key) * G::K_STRIDE + 8 * chunk;
+    cp.v_lds[i] = t * G::V_HALVES + key * D + 8 * (chunk ^ v_swizzle<D>(key));
   }
 }
 
-// Global loads of the tile pair starting at key `key0` of one head. The
-// buffer descriptors start at that key and end at key S, so the hardware
+// Buffer descriptor over keys [key0, S) of one head's K or V: the hardware
 // range check returns zeros for keys >= S.
 template <int D>
-__device__ __forceinline__ void load_pair(PairRegs<D>& r, const CopyPlan<D>& cp,
-                                          const _Float16* kh, const _Float16* vh, int key0,
-                                          int S) {
-  using G = Geometry<D>;
-  const int64_t off = (int64_t)key0 * D;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t keys_from(const _Float16* base, int key0, int S) {
   const uint32_t bytes = key0 < S ? (uint32_t)(S - key0) * D * 2 : 0u;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh + off, bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh + off, bytes);
-#pragma unroll
-  for (int i = 0; i < G::K_LOADS; ++i)
-    r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, cp.k_goff[i], 0, 0);
-#pragma unroll
-  for (int i = 0; i < G::V_LOADS; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      r.v[i][j] = __builtin_amdgcn_raw_buffer_load_b32(vrs, cp.v_goff[i] + j * D * 2, 0, 0);
+  return make_rsrc(base + (int64_t)key0 * D, bytes);
 }
 
 template <int D>
-__device__ __forceinline__ void store_pair(const PairRegs<D>& r, const CopyPlan<D>& cp,
-                                           _Float16* stage) {
-  using G = Geometry<D>;
+__device__ __forceinline__ void load_pair(PairRegs<D>& r, const CopyPlan<D>& cp,
+                                          const _Float16* base, int key0, int S) {
+  const __amdgpu_buffer_rsrc_t rs = keys_from<D>(base, key0, S);
 #pragma unroll
-  for (int i = 0; i < G::K_LOADS; ++i)
-    *reinterpret_cast<u32x4*>(stage + cp.k_lds[i]) = r.k[i];
+  for (int i = 0; i < Geometry<D>::LOADS; ++i)
+    r.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, cp.goff[i], 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void store_pair(const PairRegs<D>& r, const int (&lds)[Geometry<D>::LOADS],
+                                           _Float16* slot) {
 #pragma unroll
-  for (int i = 0; i < G::V_LOADS; ++i) {
-    // r.v[i][j] = (V[key j][d0], V[key j][d0+1]); row d0 of V^T takes the low
-    // halves of keys 0..7, row d0+1 the high halves.
-    u32x4 lo, hi;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t a = r.v[i][2 * j], b = r.v[i][2 * j + 1];
-      lo[j] = (a & 0xffffu) | (b << 16);
-      hi[j] = (a >> 16) | (b & 0xffff0000u);
-    }
-    *reinterpret_cast<u32x4*>(stage + cp.v_lds[i]) = lo;
-    *reinterpret_cast<u32x4*>(stage + cp.v_lds[i] + G::V_STRIDE) = hi;
-  }
+  for (int i = 0; i < Geometry<D>::LOADS; ++i)
+    *reinterpret_cast<u32x4*>(slot + lds[i]) = r.x[i];
+}
+
+// LDS transposing read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane n supplies the address of 4 consecutive halves X[n][0..3]; lane n
+// receives X[4e + n/4][n % 4] for e = 0..3.
+__device__ __forceinline__ f16x4 lds_read_tr(const _Float16* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(f16x4, r);
 }
 
 // Per-lane carrier of one query sub-tile (the lane's query is i = lane % 16).
@@ -221,6 +205,57 @@ struct Carrier {
   float m;                         // running max of t = s*c (base-2 units)
   float d;                         // this lane's share of the denominator
 };
+
+// S^T = K . Q^T of one tile: 4 key blocks x 2 query sub-tiles (16 MFMAs).
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x4 (&sc)[QSUB][4],
+                                        const f16x8 (&qf)[QSUB][Geometry<D>::D_CHUNKS],
+                                        const _Float16* __restrict__ ktile, int li, int g) {
+  using G = Geometry<D>;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    f16x8 a[G::D_CHUNKS];
+#pragma unroll
+    for (int ch = 0; ch < G::D_CHUNKS; ++ch)
+      a[ch] = *reinterpret_cast<const f16x8*>(ktile + (16 * kb + li) * G::K_STRIDE + 8 * g +
+                                              32 * ch);
+#pragma unroll
+    for (int qs = 0; qs < QSUB; ++qs) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ch = 0; ch < G::D_CHUNKS; ++ch)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ch], qf[qs][ch], acc, 0, 0, 0);
+      sc[qs][kb] = acc;
+    }
+  }
+}
+
+// O^T += V^T . P^T of one tile (16 MFMAs at D = 64). The A operand of d block
+// db and key chunk kc needs, in lane (i, g), V[32kc + 8g + e][16db + i] for
+// e = 0..7: two transposing reads, each over 4 key rows x 16 d, where source
+// lane n of group g points at row 32kc + 8g + 4h + n/4, halves 16db + 4(n%4).
+template <int D>
+__device__ __forceinline__ void pv_tile(Carrier<D> (&cr)[QSUB], const f16x8 (&pf)[QSUB][2],
+                                        const _Float16* __restrict__ vtile, int li, int g) {
+  using G = Geometry<D>;
+  const int row = 8 * g + (li >> 2);
+  const int sw = v_swizzle<D>(row);  // row bits that matter do not depend on kc or h
+  const _Float16* vlane = vtile + row * D + 4 * (li & 1);
+  const int x = (li & 3) >> 1;
+#pragma unroll
+  for (int db = 0; db < G::D_BLOCKS; ++db) {
+    const _Float16* vp = vlane + 8 * ((2 * db + x) ^ sw);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const f16x4 lo = lds_read_tr(vp + (32 * kc) * D);
+      const f16x4 hi = lds_read_tr(vp + (32 * kc + 4) * D);
+      const f16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs)
+        cr[qs].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[qs][kc], cr[qs].o[db], 0, 0, 0);
+    }
+  }
+}
 
 // exp2(t - m) of a 4-score accumulator, hidden keys forced to 0 when MASK.
 template <bool MASK>
@@ -235,125 +270,123 @@ __device__ __forceinline__ f32x4 exp_block(f32x4 s, float c, float m, uint32_t h
   return p;
 }
 
-// Fold one key tile (in LDS) into the wave's two carriers.
+// Online softmax of one tile's scores: probabilities (fp16, P^T operand
+// layout) into pf, denominators and, when the max moves, outputs rescaled.
 template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void fold_tile(Carrier<D> (&cr)[QSUB],
-                                          const f16x8 (&qf)[QSUB][Geometry<D>::D_CHUNKS],
-                                          const _Float16* __restrict__ tile, float c, int key0,
-                                          int qrow0, int S, int li, int g) {
+__device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB], const f32x4 (&sc)[QSUB][4],
+                                             f16x8 (&pf)[QSUB][2], float c, int key0, int qrow0,
+                                             int S, int li, int g) {
   using G = Geometry<D>;
-  const _Float16* ks = tile;
-  const _Float16* vs = tile + G::K_HALVES;
-
-  // S^T = K . Q^T: 4 key blocks x 2 query sub-tiles.
-  f32x4 sc[QSUB][4];
+  // hidden-key bits per sub-tile and key block (bit r: accumulator element r)
+  uint32_t hid[QSUB][4];
 #pragma unroll
   for (int qs = 0; qs < QSUB; ++qs)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sc[qs][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const _Float16* krow = ks + (16 * kb + li) * G::K_STRIDE + 8 * g;
-#pragma unroll
-    for (int ch = 0; ch < G::D_CHUNKS; ++ch) {
-      const f16x8 a = *reinterpret_cast<const f16x8*>(krow + 32 * ch);
-#pragma unroll
-      for (int qs = 0; qs < QSUB; ++qs)
-        sc[qs][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[qs][ch], sc[qs][kb], 0, 0, 0);
-    }
-  }
-
-  f16x8 pf[QSUB][2];
-#pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs) {
-    // hidden-key bits per key block (bit r: accumulator element r)
-    uint32_t hid[4] = {0u, 0u, 0u, 0u};
-    if (MASK) {
-      const int qrow = qrow0 + 16 * qs + li;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      hid[qs][kb] = 0u;
+      if (MASK) {
+        const int qrow = qrow0 + 16 * qs + li;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = key0 + 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
           const bool h = key >= S || (CAUSAL && key > qrow);
-          hid[kb] |= (h ? 1u : 0u) << r;
+          hid[qs][kb] |= (h ? 1u : 0u) << r;
         }
-    }
-    float m = cr[qs].m;
-    f32x4 p[4];
-    float psum;
-    auto expo = [&]() {
-      psum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) p[kb] = exp_block<MASK>(sc[qs][kb], c, m, hid[kb]);
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        f16x8 h;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          h[r] = (_Float16)p[2 * kc][r];
-          h[4 + r] = (_Float16)p[2 * kc + 1][r];
-        }
-        pf[qs][kc] = h;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          psum = __builtin_amdgcn_fdot2(f16x2{h[e], h[e + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f},
-                                        psum, false);
       }
-    };
-    expo();
-    // Lazy max: refresh m only when this tile's probabilities could overflow.
-    if (__builtin_amdgcn_ballot_w64(!(psum <= P_LIMIT)) != 0) {
+    }
+  float psum[QSUB];
+  auto expo = [&](int qs) {
+    const float m = cr[qs].m;
+    f32x4 p[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) p[kb] = exp_block<MASK>(sc[qs][kb], c, m, hid[qs][kb]);
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      f16x8 h;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        h[r] = (_Float16)p[2 * kc][r];
+        h[4 + r] = (_Float16)p[2 * kc + 1][r];
+      }
+      pf[qs][kc] = h;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        acc[(e >> 1) & 1] = __builtin_amdgcn_fdot2(
+            f16x2{h[e], h[e + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc[(e >> 1) & 1], false);
+    }
+    psum[qs] = acc[0] + acc[1];
+  };
+#pragma unroll
+  for (int qs = 0; qs < QSUB; ++qs) expo(qs);
+  // Lazy max: refresh m only when this tile's probabilities could overflow.
+  bool over = false;
+#pragma unroll
+  for (int qs = 0; qs < QSUB; ++qs) over = over || !(psum[qs] <= P_LIMIT);
+  if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+    for (int qs = 0; qs < QSUB; ++qs) {
       float tmax = NEG_BIG;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         f32x4 s = sc[qs][kb];
         if (MASK) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s[r] = ((hid[kb] >> r) & 1u) ? NEG_BIG : s[r];
+          for (int r = 0; r < 4; ++r) s[r] = ((hid[qs][kb] >> r) & 1u) ? NEG_BIG : s[r];
         }
         tmax = __builtin_fmaxf(tmax, max4(s));
       }
       tmax = group_max(tmax);
-      const float m_new = __builtin_fmaxf(m, tmax * c);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      const float m_new = __builtin_fmaxf(cr[qs].m, tmax * c);
+      const float alpha = __builtin_amdgcn_exp2f(cr[qs].m - m_new);
       cr[qs].d *= alpha;
 #pragma unroll
       for (int db = 0; db < G::D_BLOCKS; ++db) cr[qs].o[db] *= alpha;
-      m = m_new;
       cr[qs].m = m_new;
-      expo();
+      expo(qs);
     }
-    cr[qs].d += psum;
   }
+#pragma unroll
+  for (int qs = 0; qs < QSUB; ++qs) cr[qs].d += psum[qs];
+}
 
-  // O^T += V^T . P^T
-#pragma unroll
-  for (int db = 0; db < G::D_BLOCKS; ++db) {
-    const _Float16* vrow = vs + (16 * db + li) * G::V_STRIDE + 8 * g;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const f16x8 a = *reinterpret_cast<const f16x8*>(vrow + 32 * kc);
-#pragma unroll
-      for (int qs = 0; qs < QSUB; ++qs)
-        cr[qs].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[qs][kc], cr[qs].o[db], 0, 0, 0);
-    }
-  }
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void softmax_any(Carrier<D> (&cr)[QSUB], const f32x4 (&sc)[QSUB][4],
+                                            f16x8 (&pf)[QSUB][2], float c, int key0, int qrow0,
+                                            int S, int li, int g) {
+  // Element masks are needed on the sequence tail and on tiles reaching past
+  // the wave's first query (causal diagonal).
+  const bool needs_mask = (key0 + BLOCK_N > S) || (CAUSAL && key0 + BLOCK_N - 1 > qrow0);
+  if (needs_mask)
+    softmax_tile<D, CAUSAL, true>(cr, sc, pf, c, key0, qrow0, S, li, g);
+  else
+    softmax_tile<D, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
 }
 
 // grid.x = BH * n_qtiles; workgroup id -> (query tile, batch*head). The
 // heaviest (last) query tiles are issued first, which balances causal work;
 // consecutive workgroups take consecutive heads.
+//
+// Schedule. Key tiles come in pairs (2j, 2j+1); barrier interval j is one
+// trip of the main loop. Even waves own tile 2j and odd waves tile 2j+1:
+//   even, interval j: P.V of tile 2j-2, S = Q.K^T of tile 2j | softmax of 2j
+//   odd,  interval j: softmax of 2j-1 | P.V of 2j-1, S = Q.K^T of 2j+1
+// so the two waves of a SIMD alternate between MFMA-heavy and VALU-heavy
+// halves in opposite order. K of pair j must be in LDS in interval j and V of
+// pair j in interval j+1: interval j copies K of pair j+1 and V of pair j
+// (global loads at its start, LDS stores at its end) into two-slot rings.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
     int BH, int S, int n_qtiles, float c, uint32_t qsign) {
   using G = Geometry<D>;
-  __shared__ __attribute__((aligned(16))) _Float16 smem[2 * G::STAGE_HALVES];
+  __shared__ __attribute__((aligned(16))) _Float16 smem[4 * G::K_HALVES + 4 * G::V_HALVES];
+  _Float16* kring = smem;                    // [slot][tile] K tiles
+  _Float16* vring = smem + 4 * G::K_HALVES;  // [slot][tile] V^T tiles
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int li = lane & 15;
   const int g = lane >> 4;
@@ -364,8 +397,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   const int qt = n_qtiles - 1 - bid / BH;
   const int bh = bid % BH;
   const int64_t head = (int64_t)bh * S * D;
-  const uint32_t head_bytes = (uint32_t)S * D * 2;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, (uint32_t)S * D * 2);
   const _Float16* kh = k + head;
   const _Float16* vh = v + head;
 
@@ -394,35 +426,61 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
 #pragma unroll
     for (int db = 0; db < G::D_BLOCKS; ++db) cr[qs].o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // Carried across the barrier: odd waves keep a tile's scores between Q.K^T
+  // and softmax; even waves keep its fp16 probabilities between softmax and
+  // P.V, packed into the first two blocks of the same registers.
+  f32x4 sc[QSUB][4];
+  f16x8 pf[QSUB][2];
 
   const int kend = CAUSAL ? min(S, q0 + BLOCK_M) : S;
   const int n_kt = (kend + BLOCK_N - 1) / BLOCK_N;
   const int n_pairs = (n_kt + 1) / 2;
+  // tile t contributes to this wave's rows
+  auto live = [&](int t) { return t < n_kt && (!CAUSAL || t * BLOCK_N <= qrow0 + 31); };
 
   CopyPlan<D> cp;
   make_copy_plan<D>(cp, tid);
-  PairRegs<D> pr;
-  load_pair<D>(pr, cp, kh, vh, 0, S);
-  store_pair<D>(pr, cp, smem);
+  PairRegs<D> kr, vr;
+  load_pair<D>(kr, cp, kh, 0, S);
+  store_pair<D>(kr, cp.k_lds, kring);
   __syncthreads();
 
-  for (int it = 0; it < n_pairs; ++it) {
-    const bool more = it + 1 < n_pairs;
-    if (more) load_pair<D>(pr, cp, kh, vh, (it + 1) * 2 * BLOCK_N, S);
-    const int kt = 2 * it + parity;
-    const int key0 = kt * BLOCK_N;
-    const _Float16* tile = smem + (it & 1) * G::STAGE_HALVES + parity * G::TILE_HALVES;
-    // Tiles past the key range, or entirely after this wave's last query
-    // (causal), contribute nothing.
-    const bool live = kt < n_kt && (!CAUSAL || key0 <= qrow0 + 31);
-    const bool needs_mask = (key0 + BLOCK_N > S) || (CAUSAL && key0 + BLOCK_N - 1 > qrow0);
-    if (live) {
-      if (needs_mask)
-        fold_tile<D, CAUSAL, true>(cr, qf, tile, c, key0, qrow0, S, li, g);
-      else
-        fold_tile<D, CAUSAL, false>(cr, qf, tile, c, key0, qrow0, S, li, g);
+  for (int j = 0; j <= n_pairs; ++j) {
+    const bool k_next = j + 1 < n_pairs;
+    const bool v_now = j < n_pairs;
+    const _Float16* kslot = kring + (j & 1) * 2 * G::K_HALVES + parity * G::K_HALVES;
+    const _Float16* vslot = vring + ((j + 1) & 1) * 2 * G::V_HALVES + parity * G::V_HALVES;
+    const int tp = 2 * (j - 1) + parity;  // tile whose P.V is due
+    const int tc = 2 * j + parity;        // tile whose scores are due
+    const bool do_pv = j >= 1 && live(tp);
+    const bool do_qk = j < n_pairs && live(tc);
+    // MFMA half: P.V of the previous tile, then Q.K^T of this one.
+    if (do_pv) {
+#pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) pf[qs][kc] = __builtin_bit_cast(f16x8, sc[qs][kc]);
+      pv_tile<D>(cr, pf, vslot, li, g);
     }
-    if (more) store_pair<D>(pr, cp, smem + ((it + 1) & 1) * G::STAGE_HALVES);
+    if (do_qk) qk_tile<D>(sc, qf, kslot, li, g);
+    __builtin_amdgcn_sched_barrier(0);
+    // Global loads for the next interval, issued mid-interval so that the
+    // eight waves do not all queue them at once.
+    if (k_next) load_pair<D>(kr, cp, kh, (j + 1) * 2 * BLOCK_N, S);
+    if (v_now) load_pair<D>(vr, cp, vh, j * 2 * BLOCK_N, S);
+    __builtin_amdgcn_sched_barrier(0);
+    // VALU half: softmax of this tile; its probabilities wait in the score
+    // registers for the next interval's P.V.
+    if (do_qk) {
+      softmax_any<D, CAUSAL>(cr, sc, pf, c, tc * BLOCK_N, qrow0, S, li, g);
+#pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) sc[qs][kc] = __builtin_bit_cast(f32x4, pf[qs][kc]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (k_next) store_pair<D>(kr, cp.k_lds, kring + ((j + 1) & 1) * 2 * G::K_HALVES);
+    if (v_now) store_pair<D>(vr, cp.v_lds, vring + (j & 1) * 2 * G::V_HALVES);
     __syncthreads();
   }
 
