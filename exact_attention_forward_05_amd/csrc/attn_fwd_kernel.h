@@ -64,15 +64,13 @@ constexpr int QGROUPS = 4;            // waves per key-tile parity (32 rows each
 constexpr int WAVES = 2 * QGROUPS;    // even-tile and odd-tile waves
 constexpr int THREADS = WAVES * 64;
 constexpr int QSUB = 2;               // 16-row query sub-tiles per wave
-constexpr int PAD = 8;                // halves of padding per LDS row
 constexpr float NEG_BIG = -1.0e30f;   // finite stand-in for -infinity
 constexpr float P_LIMIT = 16384.0f;   // lazy-max bound on a lane's fp16 tile sum
 constexpr uint32_t BUF_FLAGS = 0x00020000u;  // raw buffer, 32-bit data format
 
 template <int D>
 struct Geometry {
-  static constexpr int K_STRIDE = D + PAD;                 // halves per K row
-  static constexpr int K_HALVES = BLOCK_N * K_STRIDE;
+  static constexpr int K_HALVES = BLOCK_N * D;             // K rows unpadded, swizzled
   static constexpr int V_HALVES = BLOCK_N * D;             // V rows unpadded, swizzled
   // two-slot rings of tile pairs for K and for V^T
   static constexpr int LDS_BYTES = (4 * K_HALVES + 4 * V_HALVES) * 2;
@@ -121,45 +119,56 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// V tile rows are stored unpadded with their 16-byte chunks permuted:
-// chunk c of key row r sits at chunk c ^ v_swizzle(r). The two-dimensional
-// XOR keeps both the 16-byte row writes and the transposing 8-byte reads of
-// the P.V operand free of LDS bank conflicts.
+// LDS tiles are unpadded with their 16-byte chunks permuted per row, so that
+// the direct global->LDS copies (which fill LDS in lane order) and every LDS
+// read pattern below are free of bank conflicts on the 64-bank LDS.
+//
+// K: row R = 16*kb + i holds key st_key(kb, i) (MFMA-row order); chunk c sits
+// at c ^ k_swizzle(R). The Q.K^T operand read has 16 lanes on 16 consecutive
+// rows at one logical chunk; the swizzle spreads them over 16 bank groups.
+template <int D>
+__device__ __forceinline__ int k_swizzle(int row) {
+  return D == 64 ? ((row >> 1) & 7) : (row & 15);
+}
+// V: row r holds key r (natural order); chunk c sits at c ^ v_swizzle(r). The
+// transposing reads of the P.V operand touch 8 rows x 32 bytes per half-wave,
+// which this swizzle maps onto distinct bank groups.
 template <int D>
 __device__ __forceinline__ int v_swizzle(int r) {
   if (D == 64) return 2 * (((r >> 1) & 1) + 2 * ((r >> 3) & 1));
   return 2 * ((r & 3) + 4 * ((r >> 3) & 1));
 }
 
-// Registers holding prefetched K or V of one tile pair on their way to LDS.
-template <int D>
-struct PairRegs {
-  u32x4 x[Geometry<D>::LOADS];
-};
-
-// Thread-constant parts of the K/V copy: byte offset of each 16-byte piece
-// relative to the first key of a tile pair (the same for K and V), and its
-// LDS destination relative to a ring slot for K and for V.
+// Direct global->LDS copy of one tile pair. A buffer load with the LDS flag
+// writes lane l's 16 bytes at M0 + 16*l, so each wave instruction fills 1 KB
+// of LDS in slot order; each lane therefore fetches the global piece that
+// belongs in its slot. Per-lane byte offsets (relative to the first key of the
+// pair) are precomputed for K and for V.
 template <int D>
 struct CopyPlan {
-  uint32_t goff[Geometry<D>::LOADS];
-  int k_lds[Geometry<D>::LOADS];
-  int v_lds[Geometry<D>::LOADS];
+  uint32_t k_off[Geometry<D>::LOADS];
+  uint32_t v_off[Geometry<D>::LOADS];
 };
 
 template <int D>
-__device__ __forceinline__ void make_copy_plan(CopyPlan<D>& cp, int tid) {
-  using G = Geometry<D>;
+__device__ __forceinline__ int copy_unit(int wave, int i) {
+  return i * WAVES + wave;  // 1 KB unit of the pair filled by instruction i of a wave
+}
+
+template <int D>
+__device__ __forceinline__ void make_copy_plan(CopyPlan<D>& cp, int wave, int lane) {
+  constexpr int CHUNKS = D / 8;                     // 16-byte chunks per row
+  constexpr int TILE_SLOTS = BLOCK_N * CHUNKS;
 #pragma unroll
-  for (int i = 0; i < G::LOADS; ++i) {
-    const int u = tid + THREADS * i;
-    const int t = u / (BLOCK_N * (D / 8));          // tile of the pair
-    const int w = u % (BLOCK_N * (D / 8));
-    const int key = w / (D / 8);
-    const int chunk = w % (D / 8);
-    cp.goff[i] = (uint32_t)(((t * BLOCK_N + key) * D + 8 * chunk) * 2);
-    cp.k_lds[i] = t * G::K_HALVES + k_row_of(key) * G::K_STRIDE + 8 * chunk;
-    cp.v_lds[i] = t * G::V_HALVES + key * D + 8 * (chunk ^ v_swizzle<D>(key));
+  for (int i = 0; i < Geometry<D>::LOADS; ++i) {
+    const int slot = copy_unit<D>(wave, i) * 64 + lane;
+    const int t = slot / TILE_SLOTS;                // tile of the pair
+    const int w = slot % TILE_SLOTS;
+    const int row = w / CHUNKS;
+    const int pc = w % CHUNKS;                       // physical chunk in the row
+    const int kkey = st_key(row >> 4, row & 15);
+    cp.k_off[i] = (uint32_t)(((t * BLOCK_N + kkey) * D + 8 * (pc ^ k_swizzle<D>(row))) * 2);
+    cp.v_off[i] = (uint32_t)(((t * BLOCK_N + row) * D + 8 * (pc ^ v_swizzle<D>(row))) * 2);
   }
 }
 
@@ -171,22 +180,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t keys_from(const _Float16* base
   return make_rsrc(base + (int64_t)key0 * D, bytes);
 }
 
+// Issue the direct copy of the tile pair starting at key0 into `slot` (the
+// pair's LDS area: tile 0 then tile 1). Completion is awaited with vmcnt.
 template <int D>
-__device__ __forceinline__ void load_pair(PairRegs<D>& r, const CopyPlan<D>& cp,
-                                          const _Float16* base, int key0, int S) {
+__device__ __forceinline__ void copy_pair(const uint32_t* off, const _Float16* base, int key0,
+                                          int S, _Float16* slot, int wave) {
   const __amdgpu_buffer_rsrc_t rs = keys_from<D>(base, key0, S);
 #pragma unroll
-  for (int i = 0; i < Geometry<D>::LOADS; ++i)
-    r.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, cp.goff[i], 0, 0);
+  for (int i = 0; i < Geometry<D>::LOADS; ++i) {
+    _Float16* dst = slot + copy_unit<D>(wave, i) * 64 * 8;   // 64 slots of 8 halves
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)dst, 16, off[i], 0, 0, 0);
+  }
 }
 
-template <int D>
-__device__ __forceinline__ void store_pair(const PairRegs<D>& r, const int (&lds)[Geometry<D>::LOADS],
-                                           _Float16* slot) {
-#pragma unroll
-  for (int i = 0; i < Geometry<D>::LOADS; ++i)
-    *reinterpret_cast<u32x4*>(slot + lds[i]) = r.x[i];
-}
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // LDS transposing read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane n supplies the address of 4 consecutive halves X[n][0..3]; lane n
@@ -212,13 +220,13 @@ __device__ __forceinline__ void qk_tile(f32x4 (&sc)[QSUB][4],
                                         const f16x8 (&qf)[QSUB][Geometry<D>::D_CHUNKS],
                                         const _Float16* __restrict__ ktile, int li, int g) {
   using G = Geometry<D>;
+  const int sw = k_swizzle<D>(li);  // the swizzle bits of row 16*kb + li do not depend on kb
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     f16x8 a[G::D_CHUNKS];
 #pragma unroll
     for (int ch = 0; ch < G::D_CHUNKS; ++ch)
-      a[ch] = *reinterpret_cast<const f16x8*>(ktile + (16 * kb + li) * G::K_STRIDE + 8 * g +
-                                              32 * ch);
+      a[ch] = *reinterpret_cast<const f16x8*>(ktile + (16 * kb + li) * D + 8 * ((4 * ch + g) ^ sw));
 #pragma unroll
     for (int qs = 0; qs < QSUB; ++qs) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -439,10 +447,9 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   auto live = [&](int t) { return t < n_kt && (!CAUSAL || t * BLOCK_N <= qrow0 + 31); };
 
   CopyPlan<D> cp;
-  make_copy_plan<D>(cp, tid);
-  PairRegs<D> kr, vr;
-  load_pair<D>(kr, cp, kh, 0, S);
-  store_pair<D>(kr, cp.k_lds, kring);
+  make_copy_plan<D>(cp, wave, lane);
+  copy_pair<D>(cp.k_off, kh, 0, S, kring, wave);
+  wait_copies();
   __syncthreads();
 
   for (int j = 0; j <= n_pairs; ++j) {
@@ -464,10 +471,12 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     }
     if (do_qk) qk_tile<D>(sc, qf, kslot, li, g);
     __builtin_amdgcn_sched_barrier(0);
-    // Global loads for the next interval, issued mid-interval so that the
-    // eight waves do not all queue them at once.
-    if (k_next) load_pair<D>(kr, cp, kh, (j + 1) * 2 * BLOCK_N, S);
-    if (v_now) load_pair<D>(vr, cp, vh, j * 2 * BLOCK_N, S);
+    // Copies for the next interval, issued mid-interval so that the eight
+    // waves do not all queue them at once.
+    if (k_next) copy_pair<D>(cp.k_off, kh, (j + 1) * 2 * BLOCK_N, S,
+                             kring + ((j + 1) & 1) * 2 * G::K_HALVES, wave);
+    if (v_now) copy_pair<D>(cp.v_off, vh, j * 2 * BLOCK_N, S, vring + (j & 1) * 2 * G::V_HALVES,
+                            wave);
     __builtin_amdgcn_sched_barrier(0);
     // VALU half: softmax of this tile; its probabilities wait in the score
     // registers for the next interval's P.V.
@@ -479,8 +488,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
         for (int kc = 0; kc < 2; ++kc) sc[qs][kc] = __builtin_bit_cast(f32x4, pf[qs][kc]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (k_next) store_pair<D>(kr, cp.k_lds, kring + ((j + 1) & 1) * 2 * G::K_HALVES);
-    if (v_now) store_pair<D>(vr, cp.v_lds, vring + (j & 1) * 2 * G::V_HALVES);
+    wait_copies();
     __syncthreads();
   }
 
