@@ -11,8 +11,10 @@ on the host as a baseline (which also checks the GPU answer).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,6 +43,40 @@ def parse():
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_forward_05_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    workload (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), or
+    None when there is none or the kernel source changed since it was taken."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    cur = kernel_source_hash()
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith(".md"):
+            continue
+        text = open(os.path.join(pdir, name)).read()
+        for block in re.findall(r"```json\n(.*?)\n```", text, flags=re.S):
+            try:
+                rec = json.loads(block)
+            except ValueError:
+                continue
+            if rec.get("workload") == workload and rec.get("source_hash") == cur:
+                return rec.get("traffic_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, sample_rows: int):
@@ -175,7 +211,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": profiled_traffic(w.name),
                      "kernel": f"attn_fwd_kernel<{w.D},{str(w.causal).lower()}>",
                      "algorithmic_flops_per_launch": w.flops,
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
