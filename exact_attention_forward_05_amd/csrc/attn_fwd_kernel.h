@@ -10,7 +10,7 @@
 //
 // Work decomposition. A workgroup of 8 waves owns BLOCK_M = 128 query rows of
 // one (batch, head). Waves 0-3 take 32 rows each and fold the even key tiles
-// (BLOCK_N = 64 keys); waves 4-7 take the same rows and fold the odd tiles.
+// (64 or 128 keys); waves 4-7 take the same rows and fold the odd tiles.
 // The two waves on one SIMD therefore work on independent data, so the MFMA
 // work of one overlaps the softmax VALU work of the other (a single wave
 // serialises its own MFMA and VALU instructions on gfx950). At the end each
@@ -41,10 +41,12 @@
 // relative precision. The row sum adds the fp16-rounded probabilities
 // (v_dot2), so d normalises exactly the weights the P.V product used.
 //
-// LDS. Two stages, each holding an even and an odd tile: K as [key][d] with
-// rows stored in MFMA-row order (row 16*kb + i holds key st_key(kb, i)) and
-// V as V^T [d][key]. Rows are padded by 8 halves, so the 16-byte reads of 16
-// consecutive rows hit 16 distinct bank groups of the 64-bank LDS.
+// LDS. K and V tiles arrive by direct global->LDS loads into two-slot rings
+// of tile pairs, V one barrier interval behind K. K rows are stored in
+// MFMA-row order (row 16*kb + i holds key st_key(kb, i)), V rows in key order;
+// both are unpadded with XOR-permuted 16-byte chunks so that every operand
+// read is free of bank conflicts on the 64-bank LDS. V^T operands come from
+// transposing LDS reads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,7 +61,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BLOCK_M = 128;          // query rows per workgroup
-constexpr int BLOCK_N = 64;           // keys per tile
 constexpr int QGROUPS = 4;            // waves per key-tile parity (32 rows each)
 constexpr int WAVES = 2 * QGROUPS;    // even-tile and odd-tile waves
 constexpr int THREADS = WAVES * 64;
@@ -70,14 +71,28 @@ constexpr uint32_t BUF_FLAGS = 0x00020000u;  // raw buffer, 32-bit data format
 
 template <int D>
 struct Geometry {
-  static constexpr int K_HALVES = BLOCK_N * D;             // K rows unpadded, swizzled
-  static constexpr int V_HALVES = BLOCK_N * D;             // V rows unpadded, swizzled
-  // two-slot rings of tile pairs for K and for V^T
-  static constexpr int LDS_BYTES = (4 * K_HALVES + 4 * V_HALVES) * 2;
+  // Keys per tile: each wave folds one tile per barrier interval. (128-key
+  // tiles would spread the fixed per-interval costs further, but the larger
+  // score block does not fit the 256-register budget of two waves per SIMD.)
+  static constexpr int BN = 64;
+  static constexpr int KB = BN / 16;                       // 16-key MFMA blocks of S^T
+  static constexpr int KC = BN / 32;                       // 32-key chunks of the P.V contraction
+  static constexpr int K_HALVES = BN * D;                  // K rows unpadded, swizzled
+  static constexpr int V_HALVES = BN * D;                  // V rows unpadded, swizzled
+  // Ring depth of tile pairs for K and for V: copies run RING-1 barrier
+  // intervals ahead of use (three slots measured slower than two at D = 64).
+  static constexpr int RING = 2;
+  static constexpr int SLOT_HALVES = 2 * K_HALVES;          // one tile pair
+  // At D = 128 the Q fragments would not fit the register budget next to the
+  // output accumulators: the workgroup's Q rows are staged in LDS instead.
+  static constexpr bool Q_IN_LDS = D == 128;
+  static constexpr int Q_HALVES = Q_IN_LDS ? BLOCK_M * D : 0;
+  static constexpr int LDS_HALVES = 2 * RING * SLOT_HALVES + Q_HALVES;
+  static constexpr int LDS_BYTES = LDS_HALVES * 2;
   static constexpr int D_CHUNKS = D / 32;                  // contraction chunks of Q.K
   static constexpr int D_BLOCKS = D / 16;                  // 16-row blocks of O^T
   // per tile pair, K and V each in 16-byte pieces
-  static constexpr int PIECES = 2 * BLOCK_N * (D / 8);
+  static constexpr int PIECES = 2 * BN * (D / 8);
   static constexpr int LOADS = PIECES / THREADS;
   static_assert(D % 64 == 0, "D must be a multiple of 64");
   static_assert(LOADS * THREADS == PIECES, "tiling");
@@ -157,8 +172,9 @@ __device__ __forceinline__ int copy_unit(int wave, int i) {
 
 template <int D>
 __device__ __forceinline__ void make_copy_plan(CopyPlan<D>& cp, int wave, int lane) {
+  using G = Geometry<D>;
   constexpr int CHUNKS = D / 8;                     // 16-byte chunks per row
-  constexpr int TILE_SLOTS = BLOCK_N * CHUNKS;
+  constexpr int TILE_SLOTS = G::BN * CHUNKS;
 #pragma unroll
   for (int i = 0; i < Geometry<D>::LOADS; ++i) {
     const int slot = copy_unit<D>(wave, i) * 64 + lane;
@@ -167,8 +183,8 @@ __device__ __forceinline__ void make_copy_plan(CopyPlan<D>& cp, int wave, int la
     const int row = w / CHUNKS;
     const int pc = w % CHUNKS;                       // physical chunk in the row
     const int kkey = st_key(row >> 4, row & 15);
-    cp.k_off[i] = (uint32_t)(((t * BLOCK_N + kkey) * D + 8 * (pc ^ k_swizzle<D>(row))) * 2);
-    cp.v_off[i] = (uint32_t)(((t * BLOCK_N + row) * D + 8 * (pc ^ v_swizzle<D>(row))) * 2);
+    cp.k_off[i] = (uint32_t)(((t * G::BN + kkey) * D + 8 * (pc ^ k_swizzle<D>(row))) * 2);
+    cp.v_off[i] = (uint32_t)(((t * G::BN + row) * D + 8 * (pc ^ v_swizzle<D>(row))) * 2);
   }
 }
 
@@ -194,7 +210,16 @@ __device__ __forceinline__ void copy_pair(const uint32_t* off, const _Float16* b
   }
 }
 
-__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N direct copies (vector memory operations) of this wave
+// are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N == 0 || N == 2 || N == 4 || N == 8, "unsupported count");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
 
 // LDS transposing read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane n supplies the address of 4 consecutive halves X[n][0..3]; lane n
@@ -214,54 +239,121 @@ struct Carrier {
   float d;                         // this lane's share of the denominator
 };
 
-// S^T = K . Q^T of one tile: 4 key blocks x 2 query sub-tiles (16 MFMAs).
-template <int D>
-__device__ __forceinline__ void qk_tile(f32x4 (&sc)[QSUB][4],
-                                        const f16x8 (&qf)[QSUB][Geometry<D>::D_CHUNKS],
-                                        const _Float16* __restrict__ ktile, int li, int g) {
-  using G = Geometry<D>;
-  const int sw = k_swizzle<D>(li);  // the swizzle bits of row 16*kb + li do not depend on kb
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    f16x8 a[G::D_CHUNKS];
-#pragma unroll
-    for (int ch = 0; ch < G::D_CHUNKS; ++ch)
-      a[ch] = *reinterpret_cast<const f16x8*>(ktile + (16 * kb + li) * D + 8 * ((4 * ch + g) ^ sw));
-#pragma unroll
-    for (int qs = 0; qs < QSUB; ++qs) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ch = 0; ch < G::D_CHUNKS; ++ch)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ch], qf[qs][ch], acc, 0, 0, 0);
-      sc[qs][kb] = acc;
-    }
+// Scheduling groups (sched_group_barrier masks): LDS reads and MFMAs.
+constexpr int SG_DS_READ = 0x100;
+constexpr int SG_MFMA = 0x008;
+// LDS read instructions of unit u: two transposing reads for a V^T fragment,
+// one 16-byte read for a K fragment.
+template <int U, int END, int NPV>
+__device__ __forceinline__ void pin_reads() {
+  if constexpr (U < END) {
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, U < NPV ? 2 : 1, 0);
+    pin_reads<U + 1, END, NPV>();
+  }
+}
+template <int U, int NU, int NPV, int AHEAD>
+__device__ __forceinline__ void pin_units() {
+  if constexpr (U < NU) {
+    if constexpr (U + AHEAD < NU)
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, U + AHEAD < NPV ? 2 : 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, QSUB, 0);
+    pin_units<U + 1, NU, NPV, AHEAD>();
   }
 }
 
-// O^T += V^T . P^T of one tile (16 MFMAs at D = 64). The A operand of d block
-// db and key chunk kc needs, in lane (i, g), V[32kc + 8g + e][16db + i] for
-// e = 0..7: two transposing reads, each over 4 key rows x 16 d, where source
-// lane n of group g points at row 32kc + 8g + 4h + n/4, halves 16db + 4(n%4).
-template <int D>
-__device__ __forceinline__ void pv_tile(Carrier<D> (&cr)[QSUB], const f16x8 (&pf)[QSUB][2],
-                                        const _Float16* __restrict__ vtile, int li, int g) {
+// The MFMA half of an interval: P.V of the previous tile (PV) and Q.K^T of the
+// current one (QK), as one software-pipelined stream of units. A unit is one
+// A-operand fragment read from LDS (two transposing reads for V^T, one 16-byte
+// read for K) and the two MFMAs (both query sub-tiles) that consume it.
+// Fragments are read AHEAD units before use, so the LDS latency is covered by
+// the MFMAs in between. Units are ordered so that consecutive MFMAs on one
+// accumulator are several instructions apart.
+template <int D, bool PV, bool QK>
+__device__ __forceinline__ void mfma_phase(Carrier<D> (&cr)[QSUB],
+                                           const f16x8 (&pf)[QSUB][Geometry<D>::KC],
+                                           f32x4 (&sc)[QSUB][Geometry<D>::KB],
+                                           const f16x8 (&qf)[QSUB][Geometry<D>::D_CHUNKS],
+                                           const _Float16* __restrict__ vtile,
+                                           const _Float16* __restrict__ ktile,
+                                           const _Float16* __restrict__ qtile, uint32_t qsign,
+                                           int li, int g) {
   using G = Geometry<D>;
-  const int row = 8 * g + (li >> 2);
-  const int sw = v_swizzle<D>(row);  // row bits that matter do not depend on kc or h
-  const _Float16* vlane = vtile + row * D + 4 * (li & 1);
-  const int x = (li & 3) >> 1;
+  constexpr int NPV = PV ? G::KC * G::D_BLOCKS : 0;
+  constexpr int NQK = QK ? G::KB * G::D_CHUNKS : 0;
+  constexpr int NU = NPV + NQK;
+  constexpr int AHEAD = (D == 64 ? 8 : 4) < NU ? (D == 64 ? 8 : 4) : NU;
+  // V^T operand (d block db, key chunk kc): lane (i, g) needs
+  // V[32kc + 8g + e][16db + i], e = 0..7 -- two transposing reads over 4 key
+  // rows x 16 d, source lane n of group g pointing at row 32kc + 8g + 4h + n/4,
+  // halves 16db + 4(n%4).
+  const int vrow = 8 * g + (li >> 2);
+  const int vsw = v_swizzle<D>(vrow);  // row bits that matter do not depend on kc or h
+  const _Float16* vlane = vtile + vrow * D + 4 * (li & 1);
+  const int vx = (li & 3) >> 1;
+  // K operand (key block kb, d chunk ch): row 16kb + li, halves 32ch + 8g.
+  const int ksw = k_swizzle<D>(li);  // the swizzle bits of row 16*kb + li do not depend on kb
+  // Q^T fragments: from registers, or (Q_IN_LDS) read from the LDS Q tile at
+  // the start of the phase -- row 16qs + li of the wave's rows, halves
+  // 32ch + 8g, chunks permuted like K rows.
+  f16x8 ql[QSUB][G::D_CHUNKS];
+  if constexpr (G::Q_IN_LDS && QK) {
 #pragma unroll
-  for (int db = 0; db < G::D_BLOCKS; ++db) {
-    const _Float16* vp = vlane + 8 * ((2 * db + x) ^ sw);
+    for (int qs = 0; qs < QSUB; ++qs)
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const f16x4 lo = lds_read_tr(vp + (32 * kc) * D);
-      const f16x4 hi = lds_read_tr(vp + (32 * kc + 4) * D);
-      const f16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int ch = 0; ch < G::D_CHUNKS; ++ch) {
+        const int row = 16 * qs + li;
+        ql[qs][ch] = *reinterpret_cast<const f16x8*>(qtile + row * D +
+                                                     8 * ((4 * ch + g) ^ k_swizzle<D>(row)));
+      }
+    if (qsign != 0u) {  // negative scale: flip Q's sign (exact)
+#pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs)
+#pragma unroll
+        for (int ch = 0; ch < G::D_CHUNKS; ++ch)
+          ql[qs][ch] = __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, ql[qs][ch]) ^ qsign);
+    }
+  }
+  auto qfrag = [&](int qs, int ch) -> const f16x8& {
+    if constexpr (G::Q_IN_LDS) return ql[qs][ch]; else return qf[qs][ch];
+  };
+  auto load = [&](int u) -> f16x8 {
+    if (u < NPV) {
+      const int kc = u / G::D_BLOCKS, db = u % G::D_BLOCKS;
+      const _Float16* vp = vlane + 8 * ((2 * db + vx) ^ vsw) + (32 * kc) * D;
+      const f16x4 lo = lds_read_tr(vp);
+      const f16x4 hi = lds_read_tr(vp + 4 * D);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const int w = u - NPV, ch = w / G::KB, kb = w % G::KB;
+    return *reinterpret_cast<const f16x8*>(ktile + (16 * kb + li) * D + 8 * ((4 * ch + g) ^ ksw));
+  };
+  auto compute = [&](int u, const f16x8& a) {
+    if (u < NPV) {
+      const int kc = u / G::D_BLOCKS, db = u % G::D_BLOCKS;
 #pragma unroll
       for (int qs = 0; qs < QSUB; ++qs)
         cr[qs].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[qs][kc], cr[qs].o[db], 0, 0, 0);
+    } else {
+      const int w = u - NPV, ch = w / G::KB, kb = w % G::KB;
+#pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs)
+        sc[qs][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            a, qfrag(qs, ch), ch == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[qs][kb], 0, 0, 0);
     }
+  };
+  f16x8 fr[NU];
+#pragma unroll
+  for (int u = 0; u < AHEAD; ++u) fr[u] = load(u);
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (u + AHEAD < NU) fr[u + AHEAD] = load(u + AHEAD);
+    compute(u, fr[u]);
+  }
+  // Pin that order for the scheduler: the reads of the first AHEAD units,
+  // then per unit the reads of unit u + AHEAD followed by unit u's two MFMAs.
+  if constexpr (D == 64) {
+    pin_reads<0, AHEAD, NPV>();
+    pin_units<0, NU, NPV, AHEAD>();
   }
 }
 
@@ -281,16 +373,17 @@ __device__ __forceinline__ f32x4 exp_block(f32x4 s, float c, float m, uint32_t h
 // Online softmax of one tile's scores: probabilities (fp16, P^T operand
 // layout) into pf, denominators and, when the max moves, outputs rescaled.
 template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB], const f32x4 (&sc)[QSUB][4],
-                                             f16x8 (&pf)[QSUB][2], float c, int key0, int qrow0,
-                                             int S, int li, int g) {
+__device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB],
+                                             const f32x4 (&sc)[QSUB][Geometry<D>::KB],
+                                             f16x8 (&pf)[QSUB][Geometry<D>::KC], float c, int key0,
+                                             int qrow0, int S, int li, int g) {
   using G = Geometry<D>;
   // hidden-key bits per sub-tile and key block (bit r: accumulator element r)
-  uint32_t hid[QSUB][4];
+  uint32_t hid[QSUB][G::KB];
 #pragma unroll
   for (int qs = 0; qs < QSUB; ++qs)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < G::KB; ++kb) {
       hid[qs][kb] = 0u;
       if (MASK) {
         const int qrow = qrow0 + 16 * qs + li;
@@ -305,12 +398,12 @@ __device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB], const f32x4
   float psum[QSUB];
   auto expo = [&](int qs) {
     const float m = cr[qs].m;
-    f32x4 p[4];
+    f32x4 p[G::KB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) p[kb] = exp_block<MASK>(sc[qs][kb], c, m, hid[qs][kb]);
+    for (int kb = 0; kb < G::KB; ++kb) p[kb] = exp_block<MASK>(sc[qs][kb], c, m, hid[qs][kb]);
     float acc[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < G::KC; ++kc) {
       f16x8 h;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -336,7 +429,7 @@ __device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB], const f32x4
     for (int qs = 0; qs < QSUB; ++qs) {
       float tmax = NEG_BIG;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < G::KB; ++kb) {
         f32x4 s = sc[qs][kb];
         if (MASK) {
 #pragma unroll
@@ -359,12 +452,14 @@ __device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB], const f32x4
 }
 
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void softmax_any(Carrier<D> (&cr)[QSUB], const f32x4 (&sc)[QSUB][4],
-                                            f16x8 (&pf)[QSUB][2], float c, int key0, int qrow0,
-                                            int S, int li, int g) {
+__device__ __forceinline__ void softmax_any(Carrier<D> (&cr)[QSUB],
+                                            const f32x4 (&sc)[QSUB][Geometry<D>::KB],
+                                            f16x8 (&pf)[QSUB][Geometry<D>::KC], float c, int key0,
+                                            int qrow0, int S, int li, int g) {
+  constexpr int BN = Geometry<D>::BN;
   // Element masks are needed on the sequence tail and on tiles reaching past
   // the wave's first query (causal diagonal).
-  const bool needs_mask = (key0 + BLOCK_N > S) || (CAUSAL && key0 + BLOCK_N - 1 > qrow0);
+  const bool needs_mask = (key0 + BN > S) || (CAUSAL && key0 + BN - 1 > qrow0);
   if (needs_mask)
     softmax_tile<D, CAUSAL, true>(cr, sc, pf, c, key0, qrow0, S, li, g);
   else
@@ -389,9 +484,11 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
     int BH, int S, int n_qtiles, float c, uint32_t qsign) {
   using G = Geometry<D>;
-  __shared__ __attribute__((aligned(16))) _Float16 smem[4 * G::K_HALVES + 4 * G::V_HALVES];
-  _Float16* kring = smem;                    // [slot][tile] K tiles
-  _Float16* vring = smem + 4 * G::K_HALVES;  // [slot][tile] V^T tiles
+  constexpr int R = G::RING;
+  __shared__ __attribute__((aligned(16))) _Float16 smem[G::LDS_HALVES];
+  _Float16* kring = smem;                           // [slot][tile] K tiles
+  _Float16* vring = smem + R * G::SLOT_HALVES;      // [slot][tile] V tiles
+  _Float16* qtile = smem + 2 * R * G::SLOT_HALVES;  // Q rows of the workgroup (Q_IN_LDS)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -412,19 +509,37 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   const int q0 = qt * BLOCK_M;
   const int qrow0 = q0 + 32 * qgrp;  // this wave's first query row
 
-  // Q^T fragments, loaded once (sign-flipped when the scale is negative).
+  // Q^T fragments, loaded once (sign-flipped when the scale is negative):
+  // into registers, or (Q_IN_LDS) the workgroup's Q rows into LDS by direct
+  // copies, chunks permuted like K rows; rows past S read as zeros.
   f16x8 qf[QSUB][G::D_CHUNKS];
+  if constexpr (G::Q_IN_LDS) {
+    constexpr int UNITS = BLOCK_M * D * 2 / 1024;  // 1 KB copy units
+    static_assert(UNITS % WAVES == 0, "Q copy split");
 #pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs) {
-    const int row = qrow0 + 16 * qs + li;
+    for (int i = 0; i < UNITS / WAVES; ++i) {
+      const int unit = i * WAVES + wave;
+      const int slot = unit * 64 + lane;
+      const int row = slot / (D / 8);
+      const int pc = slot % (D / 8);
+      const uint32_t off = (uint32_t)(((q0 + row) * D + 8 * (pc ^ k_swizzle<D>(row))) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qrs, (__attribute__((address_space(3))) void*)(qtile + unit * 512), 16, off, 0, 0, 0);
+    }
+  } else {
 #pragma unroll
-    for (int ch = 0; ch < G::D_CHUNKS; ++ch) {
-      u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-          qrs, (uint32_t)((row * D + 32 * ch + 8 * g) * 2), 0, 0);
-      w ^= qsign;
-      qf[qs][ch] = __builtin_bit_cast(f16x8, w);
+    for (int qs = 0; qs < QSUB; ++qs) {
+      const int row = qrow0 + 16 * qs + li;
+#pragma unroll
+      for (int ch = 0; ch < G::D_CHUNKS; ++ch) {
+        u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+            qrs, (uint32_t)((row * D + 32 * ch + 8 * g) * 2), 0, 0);
+        w ^= qsign;
+        qf[qs][ch] = __builtin_bit_cast(f16x8, w);
+      }
     }
   }
+  const _Float16* qwave = qtile + 32 * qgrp * D;  // this wave's rows in the LDS Q tile
 
   Carrier<D> cr[QSUB];
 #pragma unroll
@@ -437,26 +552,34 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   // Carried across the barrier: odd waves keep a tile's scores between Q.K^T
   // and softmax; even waves keep its fp16 probabilities between softmax and
   // P.V, packed into the first two blocks of the same registers.
-  f32x4 sc[QSUB][4];
-  f16x8 pf[QSUB][2];
+  f32x4 sc[QSUB][G::KB];
+  f16x8 pf[QSUB][G::KC];
 
   const int kend = CAUSAL ? min(S, q0 + BLOCK_M) : S;
-  const int n_kt = (kend + BLOCK_N - 1) / BLOCK_N;
+  const int n_kt = (kend + G::BN - 1) / G::BN;
   const int n_pairs = (n_kt + 1) / 2;
   // tile t contributes to this wave's rows
-  auto live = [&](int t) { return t < n_kt && (!CAUSAL || t * BLOCK_N <= qrow0 + 31); };
+  auto live = [&](int t) { return t < n_kt && (!CAUSAL || t * G::BN <= qrow0 + 31); };
 
   CopyPlan<D> cp;
   make_copy_plan<D>(cp, wave, lane);
-  copy_pair<D>(cp.k_off, kh, 0, S, kring, wave);
-  wait_copies();
+  // Prologue: K of pairs 0..R-2 and V of pairs 0..R-3.
+#pragma unroll
+  for (int p = 0; p < R - 1; ++p)
+    if (p < n_pairs) copy_pair<D>(cp.k_off, kh, p * 2 * G::BN, S, kring + p * G::SLOT_HALVES, wave);
+#pragma unroll
+  for (int p = 0; p < R - 2; ++p)
+    if (p < n_pairs) copy_pair<D>(cp.v_off, vh, p * 2 * G::BN, S, vring + p * G::SLOT_HALVES, wave);
+  wait_copies<0>();
   __syncthreads();
 
   for (int j = 0; j <= n_pairs; ++j) {
-    const bool k_next = j + 1 < n_pairs;
-    const bool v_now = j < n_pairs;
-    const _Float16* kslot = kring + (j & 1) * 2 * G::K_HALVES + parity * G::K_HALVES;
-    const _Float16* vslot = vring + ((j + 1) & 1) * 2 * G::V_HALVES + parity * G::V_HALVES;
+    // Interval j copies K of pair j+R-1 and V of pair j+R-2.
+    const int kp = j + R - 1, vp = j + R - 2;
+    const bool k_copy = kp < n_pairs;
+    const bool v_copy = vp < n_pairs;
+    const _Float16* kslot = kring + (j % R) * G::SLOT_HALVES + parity * G::K_HALVES;
+    const _Float16* vslot = vring + ((j + R - 1) % R) * G::SLOT_HALVES + parity * G::V_HALVES;
     const int tp = 2 * (j - 1) + parity;  // tile whose P.V is due
     const int tc = 2 * j + parity;        // tile whose scores are due
     const bool do_pv = j >= 1 && live(tp);
@@ -466,29 +589,44 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
 #pragma unroll
       for (int qs = 0; qs < QSUB; ++qs)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) pf[qs][kc] = __builtin_bit_cast(f16x8, sc[qs][kc]);
-      pv_tile<D>(cr, pf, vslot, li, g);
+        for (int kc = 0; kc < G::KC; ++kc) pf[qs][kc] = __builtin_bit_cast(f16x8, sc[qs][kc]);
     }
-    if (do_qk) qk_tile<D>(sc, qf, kslot, li, g);
+    if (do_pv && do_qk)
+      mfma_phase<D, true, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+    else if (do_pv)
+      mfma_phase<D, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+    else if (do_qk)
+      mfma_phase<D, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
     __builtin_amdgcn_sched_barrier(0);
-    // Copies for the next interval, issued mid-interval so that the eight
-    // waves do not all queue them at once.
-    if (k_next) copy_pair<D>(cp.k_off, kh, (j + 1) * 2 * BLOCK_N, S,
-                             kring + ((j + 1) & 1) * 2 * G::K_HALVES, wave);
-    if (v_now) copy_pair<D>(cp.v_off, vh, j * 2 * BLOCK_N, S, vring + (j & 1) * 2 * G::V_HALVES,
-                            wave);
+    // Copies for later intervals, issued mid-interval so that the eight waves
+    // do not all queue them at once.
+    if (k_copy) copy_pair<D>(cp.k_off, kh, kp * 2 * G::BN, S, kring + (kp % R) * G::SLOT_HALVES,
+                             wave);
+    if (v_copy) copy_pair<D>(cp.v_off, vh, vp * 2 * G::BN, S, vring + (vp % R) * G::SLOT_HALVES,
+                             wave);
     __builtin_amdgcn_sched_barrier(0);
     // VALU half: softmax of this tile; its probabilities wait in the score
     // registers for the next interval's P.V.
     if (do_qk) {
-      softmax_any<D, CAUSAL>(cr, sc, pf, c, tc * BLOCK_N, qrow0, S, li, g);
+      softmax_any<D, CAUSAL>(cr, sc, pf, c, tc * G::BN, qrow0, S, li, g);
 #pragma unroll
       for (int qs = 0; qs < QSUB; ++qs)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) sc[qs][kc] = __builtin_bit_cast(f32x4, pf[qs][kc]);
+        for (int kc = 0; kc < G::KC; ++kc) sc[qs][kc] = __builtin_bit_cast(f32x4, pf[qs][kc]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    wait_copies();
+    // What interval j+1 reads was copied R-2 intervals ago: only this
+    // interval's copies may stay in flight.
+    if constexpr (R == 2) {
+      wait_copies<0>();
+    } else {
+      if (k_copy && v_copy)
+        wait_copies<2 * G::LOADS>();
+      else if (k_copy || v_copy)
+        wait_copies<G::LOADS>();
+      else
+        wait_copies<0>();
+    }
     __syncthreads();
   }
 
