@@ -79,9 +79,13 @@ struct Geometry {
   static constexpr int KC = BN / 32;                       // 32-key chunks of the P.V contraction
   static constexpr int K_HALVES = BN * D;                  // K rows unpadded, swizzled
   static constexpr int V_HALVES = BN * D;                  // V rows unpadded, swizzled
-  // Ring depth of tile pairs for K and for V: copies run RING-1 barrier
-  // intervals ahead of use (three slots measured slower than two at D = 64).
-  static constexpr int RING = 2;
+  // Tile pairs (even tile for the even waves, odd tile for the odd waves)
+  // folded per barrier interval. Two per interval (rings of four pairs) were
+  // measured 1-2% slower at D = 64 than one: the barrier is not what limits.
+  static constexpr int TPI = 1;
+  // Rings of 2*TPI tile pairs for K and for V: TPI pairs are read while the
+  // next TPI pairs are copied.
+  static constexpr int RING = 2 * TPI;
   static constexpr int SLOT_HALVES = 2 * K_HALVES;          // one tile pair
   // At D = 128 the Q fragments would not fit the register budget next to the
   // output accumulators: the workgroup's Q rows are staged in LDS instead.
@@ -470,14 +474,11 @@ __device__ __forceinline__ void softmax_any(Carrier<D> (&cr)[QSUB],
 // heaviest (last) query tiles are issued first, which balances causal work;
 // consecutive workgroups take consecutive heads.
 //
-// Schedule. Key tiles come in pairs (2j, 2j+1); barrier interval j is one
-// trip of the main loop. Even waves own tile 2j and odd waves tile 2j+1:
-//   even, interval j: P.V of tile 2j-2, S = Q.K^T of tile 2j | softmax of 2j
-//   odd,  interval j: softmax of 2j-1 | P.V of 2j-1, S = Q.K^T of 2j+1
-// so the two waves of a SIMD alternate between MFMA-heavy and VALU-heavy
-// halves in opposite order. K of pair j must be in LDS in interval j and V of
-// pair j in interval j+1: interval j copies K of pair j+1 and V of pair j
-// (global loads at its start, LDS stores at its end) into two-slot rings.
+// Schedule. Key tiles come in pairs (2p, 2p+1): even waves fold tile 2p and
+// odd waves tile 2p+1. Barrier interval j is one trip of the main loop and
+// takes TPI steps; each step is an MFMA phase (P.V of the wave's previous
+// tile, Q.K^T of its next one) followed by the softmax of the tile just
+// scored. K and V reach LDS by direct copies one interval ahead of use.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
@@ -557,76 +558,79 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
 
   const int kend = CAUSAL ? min(S, q0 + BLOCK_M) : S;
   const int n_kt = (kend + G::BN - 1) / G::BN;
+  constexpr int TPI = G::TPI;
   const int n_pairs = (n_kt + 1) / 2;
+  // P.V of pair p runs one step after its scores, so the last pair's P.V
+  // needs one more step than there are pairs.
+  const int n_intervals = (n_pairs + TPI) / TPI;
   // tile t contributes to this wave's rows
   auto live = [&](int t) { return t < n_kt && (!CAUSAL || t * G::BN <= qrow0 + 31); };
+  auto kslot_of = [&](int p) { return kring + (p % R) * G::SLOT_HALVES + parity * G::K_HALVES; };
+  auto vslot_of = [&](int p) { return vring + (p % R) * G::SLOT_HALVES + parity * G::V_HALVES; };
 
   CopyPlan<D> cp;
   make_copy_plan<D>(cp, wave, lane);
-  // Prologue: K of pairs 0..R-2 and V of pairs 0..R-3.
+  // Prologue: K of pairs 0..TPI-1 and V of pairs 0..TPI-2.
 #pragma unroll
-  for (int p = 0; p < R - 1; ++p)
-    if (p < n_pairs) copy_pair<D>(cp.k_off, kh, p * 2 * G::BN, S, kring + p * G::SLOT_HALVES, wave);
-#pragma unroll
-  for (int p = 0; p < R - 2; ++p)
-    if (p < n_pairs) copy_pair<D>(cp.v_off, vh, p * 2 * G::BN, S, vring + p * G::SLOT_HALVES, wave);
+  for (int u = 0; u < TPI; ++u) {
+    if (u < n_pairs) copy_pair<D>(cp.k_off, kh, 2 * u * G::BN, S, kring + u * G::SLOT_HALVES, wave);
+    if (u + 1 < TPI && u < n_pairs)
+      copy_pair<D>(cp.v_off, vh, 2 * u * G::BN, S, vring + u * G::SLOT_HALVES, wave);
+  }
   wait_copies<0>();
   __syncthreads();
 
-  for (int j = 0; j <= n_pairs; ++j) {
-    // Interval j copies K of pair j+R-1 and V of pair j+R-2.
-    const int kp = j + R - 1, vp = j + R - 2;
-    const bool k_copy = kp < n_pairs;
-    const bool v_copy = vp < n_pairs;
-    const _Float16* kslot = kring + (j % R) * G::SLOT_HALVES + parity * G::K_HALVES;
-    const _Float16* vslot = vring + ((j + R - 1) % R) * G::SLOT_HALVES + parity * G::V_HALVES;
-    const int tp = 2 * (j - 1) + parity;  // tile whose P.V is due
-    const int tc = 2 * j + parity;        // tile whose scores are due
-    const bool do_pv = j >= 1 && live(tp);
-    const bool do_qk = j < n_pairs && live(tc);
-    // MFMA half: P.V of the previous tile, then Q.K^T of this one.
-    if (do_pv) {
+  // Interval j, step u: P.V of pair TPI*j+u-1 and Q.K^T of pair TPI*j+u (MFMA),
+  // then the softmax of the pair just scored (VALU), so the probabilities go
+  // from registers straight into the next step's P.V. Interval j reads K of
+  // pairs [TPI*j, TPI*j+TPI) and V of pairs [TPI*j-1, TPI*j+TPI-1); it copies
+  // K and V of the next TPI pairs of each into the ring positions that held
+  // pairs read in interval j-1 (the ring holds 2*TPI pairs).
+  auto issue_copies = [&](int j, int u) {
+    const int kp = TPI * (j + 1) + u;
+    const int vp = TPI * j + TPI - 1 + u;
+    if (kp < n_pairs)
+      copy_pair<D>(cp.k_off, kh, 2 * kp * G::BN, S, kring + (kp % R) * G::SLOT_HALVES, wave);
+    if (vp < n_pairs)
+      copy_pair<D>(cp.v_off, vh, 2 * vp * G::BN, S, vring + (vp % R) * G::SLOT_HALVES, wave);
+  };
+  for (int j = 0; j < n_intervals; ++j) {
 #pragma unroll
-      for (int qs = 0; qs < QSUB; ++qs)
+    for (int u = 0; u < TPI; ++u) {
+      const int pq = TPI * j + u;                    // pair whose scores are due
+      const int tp = 2 * (pq - 1) + parity;          // tile whose P.V is due
+      const int tc = 2 * pq + parity;                // tile whose scores are due
+      const bool do_pv = pq >= 1 && live(tp);
+      const bool do_qk = live(tc);
+      const _Float16* vslot = vslot_of(pq + R - 1);  // pair pq-1, kept non-negative
+      const _Float16* kslot = kslot_of(pq);
+      if (do_pv) {
 #pragma unroll
-        for (int kc = 0; kc < G::KC; ++kc) pf[qs][kc] = __builtin_bit_cast(f16x8, sc[qs][kc]);
+        for (int qs = 0; qs < QSUB; ++qs)
+#pragma unroll
+          for (int kc = 0; kc < G::KC; ++kc) pf[qs][kc] = __builtin_bit_cast(f16x8, sc[qs][kc]);
+      }
+      if (do_pv && do_qk)
+        mfma_phase<D, true, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+      else if (do_pv)
+        mfma_phase<D, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+      else if (do_qk)
+        mfma_phase<D, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+      __builtin_amdgcn_sched_barrier(0);
+      // Copies for the next interval, issued between the MFMA phase (whose LDS
+      // reads they would slow) and the softmax (which does not touch LDS).
+      issue_copies(j, u);
+      __builtin_amdgcn_sched_barrier(0);
+      if (do_qk) {
+        softmax_any<D, CAUSAL>(cr, sc, pf, c, tc * G::BN, qrow0, S, li, g);
+#pragma unroll
+        for (int qs = 0; qs < QSUB; ++qs)
+#pragma unroll
+          for (int kc = 0; kc < G::KC; ++kc) sc[qs][kc] = __builtin_bit_cast(f32x4, pf[qs][kc]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (do_pv && do_qk)
-      mfma_phase<D, true, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
-    else if (do_pv)
-      mfma_phase<D, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
-    else if (do_qk)
-      mfma_phase<D, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
-    __builtin_amdgcn_sched_barrier(0);
-    // Copies for later intervals, issued mid-interval so that the eight waves
-    // do not all queue them at once.
-    if (k_copy) copy_pair<D>(cp.k_off, kh, kp * 2 * G::BN, S, kring + (kp % R) * G::SLOT_HALVES,
-                             wave);
-    if (v_copy) copy_pair<D>(cp.v_off, vh, vp * 2 * G::BN, S, vring + (vp % R) * G::SLOT_HALVES,
-                             wave);
-    __builtin_amdgcn_sched_barrier(0);
-    // VALU half: softmax of this tile; its probabilities wait in the score
-    // registers for the next interval's P.V.
-    if (do_qk) {
-      softmax_any<D, CAUSAL>(cr, sc, pf, c, tc * G::BN, qrow0, S, li, g);
-#pragma unroll
-      for (int qs = 0; qs < QSUB; ++qs)
-#pragma unroll
-        for (int kc = 0; kc < G::KC; ++kc) sc[qs][kc] = __builtin_bit_cast(f32x4, pf[qs][kc]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // What interval j+1 reads was copied R-2 intervals ago: only this
-    // interval's copies may stay in flight.
-    if constexpr (R == 2) {
-      wait_copies<0>();
-    } else {
-      if (k_copy && v_copy)
-        wait_copies<2 * G::LOADS>();
-      else if (k_copy || v_copy)
-        wait_copies<G::LOADS>();
-      else
-        wait_copies<0>();
-    }
+    wait_copies<0>();
     __syncthreads();
   }
 
