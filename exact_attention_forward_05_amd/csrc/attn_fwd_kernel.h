@@ -52,6 +52,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -79,13 +81,11 @@ struct Geometry {
   static constexpr int KC = BN / 32;                       // 32-key chunks of the P.V contraction
   static constexpr int K_HALVES = BN * D;                  // K rows unpadded, swizzled
   static constexpr int V_HALVES = BN * D;                  // V rows unpadded, swizzled
-  // Tile pairs (even tile for the even waves, odd tile for the odd waves)
-  // folded per barrier interval. Two per interval (rings of four pairs) were
-  // measured 1-2% slower at D = 64 than one: the barrier is not what limits.
-  static constexpr int TPI = 1;
-  // Rings of 2*TPI tile pairs for K and for V: TPI pairs are read while the
-  // next TPI pairs are copied.
-  static constexpr int RING = 2 * TPI;
+  // Two-slot rings of tile pairs (even tile for the even waves, odd tile for
+  // the odd waves) for K and for V: one pair is read while the next is
+  // copied. (Deeper rings, and two pairs per barrier interval, measured no
+  // faster.)
+  static constexpr int RING = 2;
   static constexpr int SLOT_HALVES = 2 * K_HALVES;          // one tile pair
   // At D = 128 the Q fragments would not fit the register budget next to the
   // output accumulators: the workgroup's Q rows are staged in LDS instead.
@@ -475,10 +475,10 @@ __device__ __forceinline__ void softmax_any(Carrier<D> (&cr)[QSUB],
 // consecutive workgroups take consecutive heads.
 //
 // Schedule. Key tiles come in pairs (2p, 2p+1): even waves fold tile 2p and
-// odd waves tile 2p+1. Barrier interval j is one trip of the main loop and
-// takes TPI steps; each step is an MFMA phase (P.V of the wave's previous
-// tile, Q.K^T of its next one) followed by the softmax of the tile just
-// scored. K and V reach LDS by direct copies one interval ahead of use.
+// odd waves tile 2p+1. Each barrier interval is an MFMA phase (P.V of the
+// wave's previous tile, Q.K^T of its next one) followed by the softmax of the
+// tile just scored. K and V reach LDS by direct copies one interval ahead of
+// use.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
@@ -550,89 +550,73 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
 #pragma unroll
     for (int db = 0; db < G::D_BLOCKS; ++db) cr[qs].o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // Carried across the barrier: odd waves keep a tile's scores between Q.K^T
-  // and softmax; even waves keep its fp16 probabilities between softmax and
-  // P.V, packed into the first two blocks of the same registers.
-  f32x4 sc[QSUB][G::KB];
+  // fp16 probabilities of the wave's last scored tile, carried across the
+  // barrier into the next interval's P.V; sc holds a tile's scores between
+  // Q.K^T and softmax within one interval.
   f16x8 pf[QSUB][G::KC];
+  f32x4 sc[QSUB][G::KB];
 
   const int kend = CAUSAL ? min(S, q0 + BLOCK_M) : S;
   const int n_kt = (kend + G::BN - 1) / G::BN;
-  constexpr int TPI = G::TPI;
   const int n_pairs = (n_kt + 1) / 2;
-  // P.V of pair p runs one step after its scores, so the last pair's P.V
-  // needs one more step than there are pairs.
-  const int n_intervals = (n_pairs + TPI) / TPI;
-  // tile t contributes to this wave's rows
-  auto live = [&](int t) { return t < n_kt && (!CAUSAL || t * G::BN <= qrow0 + 31); };
-  auto kslot_of = [&](int p) { return kring + (p % R) * G::SLOT_HALVES + parity * G::K_HALVES; };
-  auto vslot_of = [&](int p) { return vring + (p % R) * G::SLOT_HALVES + parity * G::V_HALVES; };
+  // Pairs whose tile of this wave's parity holds keys for its rows: a prefix,
+  // since tiles past S or past the wave's last query (causal) are skipped.
+  const int row_end = CAUSAL ? min(kend, qrow0 + 32) : kend;  // keys < row_end are needed
+  const int live_tiles = (row_end + G::BN - 1) / G::BN;
+  const int n_live = (live_tiles - parity + 1) / 2;
+  // Only the last live pair of a wave can need element masks: the sequence
+  // tail is in the last tile, and a tile crossing the causal diagonal of the
+  // wave's 32 rows is the last one at or below them.
 
   CopyPlan<D> cp;
   make_copy_plan<D>(cp, wave, lane);
-  // Prologue: K of pairs 0..TPI-1 and V of pairs 0..TPI-2.
-#pragma unroll
-  for (int u = 0; u < TPI; ++u) {
-    if (u < n_pairs) copy_pair<D>(cp.k_off, kh, 2 * u * G::BN, S, kring + u * G::SLOT_HALVES, wave);
-    if (u + 1 < TPI && u < n_pairs)
-      copy_pair<D>(cp.v_off, vh, 2 * u * G::BN, S, vring + u * G::SLOT_HALVES, wave);
-  }
+  copy_pair<D>(cp.k_off, kh, 0, S, kring, wave);  // K of pair 0
   wait_copies<0>();
   __syncthreads();
 
-  // Interval j, step u: P.V of pair TPI*j+u-1 and Q.K^T of pair TPI*j+u (MFMA),
-  // then the softmax of the pair just scored (VALU), so the probabilities go
-  // from registers straight into the next step's P.V. Interval j reads K of
-  // pairs [TPI*j, TPI*j+TPI) and V of pairs [TPI*j-1, TPI*j+TPI-1); it copies
-  // K and V of the next TPI pairs of each into the ring positions that held
-  // pairs read in interval j-1 (the ring holds 2*TPI pairs).
-  auto issue_copies = [&](int j, int u) {
-    const int kp = TPI * (j + 1) + u;
-    const int vp = TPI * j + TPI - 1 + u;
-    if (kp < n_pairs)
-      copy_pair<D>(cp.k_off, kh, 2 * kp * G::BN, S, kring + (kp % R) * G::SLOT_HALVES, wave);
-    if (vp < n_pairs)
-      copy_pair<D>(cp.v_off, vh, 2 * vp * G::BN, S, vring + (vp % R) * G::SLOT_HALVES, wave);
-  };
-  for (int j = 0; j < n_intervals; ++j) {
-#pragma unroll
-    for (int u = 0; u < TPI; ++u) {
-      const int pq = TPI * j + u;                    // pair whose scores are due
-      const int tp = 2 * (pq - 1) + parity;          // tile whose P.V is due
-      const int tc = 2 * pq + parity;                // tile whose scores are due
-      const bool do_pv = pq >= 1 && live(tp);
-      const bool do_qk = live(tc);
-      const _Float16* vslot = vslot_of(pq + R - 1);  // pair pq-1, kept non-negative
-      const _Float16* kslot = kslot_of(pq);
-      if (do_pv) {
-#pragma unroll
-        for (int qs = 0; qs < QSUB; ++qs)
-#pragma unroll
-          for (int kc = 0; kc < G::KC; ++kc) pf[qs][kc] = __builtin_bit_cast(f16x8, sc[qs][kc]);
-      }
-      if (do_pv && do_qk)
-        mfma_phase<D, true, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
-      else if (do_pv)
-        mfma_phase<D, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
-      else if (do_qk)
-        mfma_phase<D, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
-      __builtin_amdgcn_sched_barrier(0);
-      // Copies for the next interval, issued between the MFMA phase (whose LDS
-      // reads they would slow) and the softmax (which does not touch LDS).
-      issue_copies(j, u);
-      __builtin_amdgcn_sched_barrier(0);
-      if (do_qk) {
-        softmax_any<D, CAUSAL>(cr, sc, pf, c, tc * G::BN, qrow0, S, li, g);
-#pragma unroll
-        for (int qs = 0; qs < QSUB; ++qs)
-#pragma unroll
-          for (int kc = 0; kc < G::KC; ++kc) sc[qs][kc] = __builtin_bit_cast(f32x4, pf[qs][kc]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+  // Barrier interval j: P.V of pair j-1 and Q.K^T of pair j (MFMA), then the
+  // copies of K of pair j+1 and V of pair j, then the softmax of pair j
+  // (VALU); the probabilities stay in registers for interval j+1. The copies
+  // sit between the MFMA phase (whose LDS reads they would slow) and the
+  // softmax (which does not touch LDS). K of pair j is read from ring slot
+  // j % 2 and V of pair j-1 from slot (j-1) % 2, both copied in interval
+  // j-1. Every wave runs all n_pairs + 1 intervals; the body is specialised
+  // (compile-time flags) so that the steady state has no branches.
+  auto interval = [&](int j, auto pv_flag, auto qk_flag, auto edge_flag) {
+    constexpr bool PV = decltype(pv_flag)::value;
+    constexpr bool QK = decltype(qk_flag)::value;
+    constexpr bool EDGE = decltype(edge_flag)::value;  // the tile may need masks
+    const _Float16* kslot = kring + (j & 1) * G::SLOT_HALVES + parity * G::K_HALVES;
+    const _Float16* vslot = vring + ((j + 1) & 1) * G::SLOT_HALVES + parity * G::V_HALVES;
+    if constexpr (PV || QK) mfma_phase<D, PV, QK>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 < n_pairs)
+      copy_pair<D>(cp.k_off, kh, 2 * (j + 1) * G::BN, S, kring + ((j + 1) & 1) * G::SLOT_HALVES, wave);
+    if (j < n_pairs)
+      copy_pair<D>(cp.v_off, vh, 2 * j * G::BN, S, vring + (j & 1) * G::SLOT_HALVES, wave);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (QK) {
+      const int key0 = (2 * j + parity) * G::BN;
+      if constexpr (EDGE)
+        softmax_any<D, CAUSAL>(cr, sc, pf, c, key0, qrow0, S, li, g);
+      else
+        softmax_tile<D, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
     }
+    __builtin_amdgcn_sched_barrier(0);
     wait_copies<0>();
     __syncthreads();
-  }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int j = 0;
+  if (n_live >= 1)
+    interval(j++, F_{}, T_{}, T_{});
+  else
+    interval(j++, F_{}, F_{}, F_{});
+  for (; j + 1 < n_live; ++j) interval(j, T_{}, T_{}, F_{});  // steady state
+  if (j + 1 == n_live) interval(j++, T_{}, T_{}, T_{});       // last live pair
+  if (j == n_live && j >= 1) interval(j++, T_{}, F_{}, F_{}); // its P.V
+  for (; j <= n_pairs; ++j) interval(j, F_{}, F_{}, F_{});    // idle: copies and barriers
 
   // Odd-tile waves hand their carriers to their even-tile partners.
   float* xfer = reinterpret_cast<float*>(smem) + qgrp * 64 * G::CARRIER_FLOATS + lane;
