@@ -38,6 +38,10 @@ def parse():
                     help="rows per head for the CPU leg (0 = every row)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the sequence-length sweep (4k/8k/16k, B1 H8 D64)")
+    ap.add_argument("--sweep-steps", type=int, default=30,
+                    help="timed launches per sweep point")
     return ap.parse_args()
 
 
@@ -123,6 +127,56 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, sample_rows: int):
             "note": "fp64 numpy oracle; matmuls on BLAS threads, exp/max/sum single-threaded"}, parity
 
 
+def time_launches(step, stream, steps):
+    """Launch ``step`` ``steps`` times, each bracketed by HIP events on the
+    launch stream; returns (per-launch ms array, wall seconds)."""
+    import torch
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]), wall
+
+
+def run_sweep(attn, dev, stream, steps):
+    """Kernel time over the sequence-length sweep (B1 H8 D64; S = 4k, 8k, 16k;
+    non-causal and causal)."""
+    import torch
+
+    from testkit import SWEEP, WORKLOADS, workload_inputs
+
+    out = []
+    for (S, causal), name in sorted(SWEEP.items(), key=lambda kv: (kv[0][1], kv[0][0])):
+        w = WORKLOADS[name]
+        q, k, v = (torch.from_numpy(x).to(dev) for x in workload_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+
+        def step():
+            attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+
+        for _ in range(5):
+            step()
+        durs, _ = time_launches(step, stream, steps)
+        mean_ms = float(durs.mean())
+        out.append({"workload": name, "S": S, "causal": causal,
+                    "us_mean": round(mean_ms * 1e3, 3),
+                    "us_median": round(float(np.median(durs)) * 1e3, 3),
+                    "tflops": round(w.flops / (mean_ms * 1e-3) / 1e12, 2),
+                    "pct_of_peak": round(100 * w.flops / (mean_ms * 1e-3) / 1e12
+                                         / PEAK_FP16_MFMA_TFLOPS, 2)})
+        log(f"sweep {name}: {out[-1]['us_mean']} us, {out[-1]['tflops']} TFLOP/s")
+        del q, k, v, o, lse
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -170,17 +224,7 @@ def main():
     log(f"warmup {args.warmup} done")
 
     # Per-launch device time from events recorded on the launch stream.
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    durs_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    durs_ms, wall = time_launches(step, stream, args.steps)
     avg_ms = float(durs_ms.mean())
     log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms, kernel avg {avg_ms * 1e3:.2f} us, "
         f"median {np.median(durs_ms) * 1e3:.2f} us, min {durs_ms.min() * 1e3:.2f} us")
@@ -218,6 +262,8 @@ def main():
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }
+    if not args.no_sweep:
+        result["sweep"] = run_sweep(attn, dev, stream, args.sweep_steps)
     if not args.no_cpu_baseline:
         log("CPU oracle leg ...")
         o_np = o.cpu().numpy()

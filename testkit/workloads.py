@@ -5,7 +5,10 @@ Way, Part 2, workload definitions: SDPA_L = [1,4,128,64] for listings and
 SDPA_P = [1,8,4096,64] for timing, fp16 Q/K/V in [B,H,S,D] from randn, default
 scale 1/sqrt(D)), widened with a long-sequence case, two causal cases at
 head_dim 128, and one with Q and K drawn three times wider so the softmax is
-peaked and the running max moves often.
+peaked and the running max moves often. A sweep over sequence lengths 4k, 8k
+and 16k (batch 1, 8 heads, head_dim 64, with and without the causal mask)
+follows the sequence lengths at which "Three kernels for a chip the ecosystem
+skipped" (Kernel one: FlashAttention-2) reports its attention throughput.
 
 Q, K and V use generator streams 0, 1 and 2 under the workload's seed.
 """
@@ -66,9 +69,26 @@ WORKLOADS = {
     "causal_b2h16s8192d128": Workload("causal_b2h16s8192d128", 2, 16, 8192, 128, True, SEED_BASE + 4),
     "peaked_causal_b4h32s4096d128": Workload(
         "peaked_causal_b4h32s4096d128", 4, 32, 4096, 128, True, SEED_BASE + 5, qk_mult=3.0),
+    "sweep_b1h8s8192d64": Workload("sweep_b1h8s8192d64", 1, 8, 8192, 64, False, SEED_BASE + 6),
+    "sweep_causal_b1h8s4096d64": Workload(
+        "sweep_causal_b1h8s4096d64", 1, 8, 4096, 64, True, SEED_BASE + 7),
+    "sweep_causal_b1h8s8192d64": Workload(
+        "sweep_causal_b1h8s8192d64", 1, 8, 8192, 64, True, SEED_BASE + 8),
+    "sweep_causal_b1h8s16384d64": Workload(
+        "sweep_causal_b1h8s16384d64", 1, 8, 16384, 64, True, SEED_BASE + 9),
 }
 
 HEADLINE = "sdpa_b1h8s4096d64"
+
+# Sequence-length sweep at batch 1, 8 heads, head_dim 64: (S, causal) -> name.
+SWEEP = {
+    (4096, False): "sdpa_b1h8s4096d64",
+    (8192, False): "sweep_b1h8s8192d64",
+    (16384, False): "long_b1h8s16384d64",
+    (4096, True): "sweep_causal_b1h8s4096d64",
+    (8192, True): "sweep_causal_b1h8s8192d64",
+    (16384, True): "sweep_causal_b1h8s16384d64",
+}
 
 
 def make_qkv(B: int, H: int, S: int, D: int, seed: int,
