@@ -12,6 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libattn_fwd.so")
 
 ATTN_OK = 0
+MAX_SPLITS = 64  # ATTN_MAX_SPLITS
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
                 4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_ARG", 6: "ATTN_ERR_HIP"}
 
@@ -21,6 +22,12 @@ _SIGNATURES = [
      [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
       ctypes.c_void_p]),
+    ("attn_fwd_splitkv", ctypes.c_int,
+     [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+      ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("attn_fwd_splitkv_workspace_size", ctypes.c_size_t,
+     [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     ("attn_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("attn_last_error", ctypes.c_char_p, []),
     ("attn_version", ctypes.c_int, []),
@@ -62,3 +69,17 @@ def attn_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: in
     """Raw call of the C entry point with integer addresses; returns the status."""
     return load().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D,
                            ctypes.c_float(scale), causal, stream)
+
+
+def attn_fwd_splitkv(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
+                     S: int, D: int, scale: float, causal: int, n_splits: int, ws_ptr: int,
+                     ws_bytes: int, stream: int) -> int:
+    """Raw call of the split-KV entry point with integer addresses; returns the status."""
+    return load().attn_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D,
+                                   ctypes.c_float(scale), causal, n_splits, ws_ptr, ws_bytes,
+                                   stream)
+
+
+def splitkv_workspace_size(B: int, H: int, S: int, D: int, n_splits: int) -> int:
+    """Bytes of workspace attn_fwd_splitkv needs (0 for n_splits == 1 or bad arguments)."""
+    return int(load().attn_fwd_splitkv_workspace_size(B, H, S, D, n_splits))

@@ -5,8 +5,10 @@ in the HIP kernels behind the C ABI.
 """
 from __future__ import annotations
 
+import functools
+import heapq
 import math
-from typing import Optional, Tuple
+from typing import Optional, Tuple, Union
 
 import torch
 
@@ -18,17 +20,8 @@ def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
-def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
-        causal: bool = False, out: Optional[torch.Tensor] = None,
-        lse: Optional[torch.Tensor] = None,
-        stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Exact attention forward on the GPU.
-
-    q, k, v: fp16 CUDA tensors of one shape [B, H, S, D], contiguous, D in {64, 128}.
-    Returns (o, lse): o fp16 [B, H, S, D] and lse fp32 [B, H, S] (natural log).
-    ``out``/``lse`` may be preallocated. The call is asynchronous on ``stream``
-    (default: torch's current stream).
-    """
+def _prepare(q, k, v, scale, out, lse, stream):
+    """Checks and output allocation shared by the entry points."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError(f"{name} must be a CUDA tensor")
@@ -57,9 +50,104 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float
         raise ValueError("lse must be a contiguous fp32 tensor [B,H,S] on q's device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    return B, H, S, D, float(scale), out, lse, stream
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+        causal: bool = False, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None,
+        stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact attention forward on the GPU.
+
+    q, k, v: fp16 CUDA tensors of one shape [B, H, S, D], contiguous, D in {64, 128}.
+    Returns (o, lse): o fp16 [B, H, S, D] and lse fp32 [B, H, S] (natural log).
+    ``out``/``lse`` may be preallocated. The call is asynchronous on ``stream``
+    (default: torch's current stream).
+    """
+    B, H, S, D, scale, out, lse, stream = _prepare(q, k, v, scale, out, lse, stream)
     with torch.cuda.device(q.device):
         st = _lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                           lse.data_ptr(), B, H, S, D, float(scale), int(bool(causal)),
+                           lse.data_ptr(), B, H, S, D, scale, int(bool(causal)),
                            stream.cuda_stream)
+    _lib.check(st)
+    return out, lse
+
+
+BLOCK_M = 128     # query rows per workgroup
+PAIR_KEYS = 128   # keys per tile pair (two 64-key tiles)
+# Rough per-interval time (one tile pair per wave) and HBM rate used to price
+# the combine; only the choice between split counts depends on them.
+_INTERVAL_US = {64: 1.4, 128: 2.4}
+_COMBINE_GBS = 4000.0
+_COMBINE_FIXED_US = 4.0
+_SPLIT_CHOICES = (1, 2, 3, 4, 6, 8, 12, 16)
+
+
+@functools.lru_cache(maxsize=256)
+def choose_splits(B: int, H: int, S: int, D: int, causal: bool, n_cus: int = 256) -> int:
+    """Split count for attn_fwd_splitkv from a small cost model.
+
+    Each workgroup (one per CU: its LDS use allows no second) costs its run of
+    tile pairs plus two intervals of fixed work; workgroups are placed longest
+    first on the least loaded CU; a split count above one adds the partial
+    results' HBM traffic and a second launch. Returns the cheapest count.
+    """
+    n_qt = -(-S // BLOCK_M)
+    pairs = [-(-min(S, BLOCK_M * (i + 1) if causal else S) // PAIR_KEYS) for i in range(n_qt)]
+    if B * H * n_qt >= 4 * n_cus and not causal:
+        return 1
+    best, best_us = 1, math.inf
+    for s in _SPLIT_CHOICES:
+        if s > max(pairs):
+            break
+        costs = []
+        for p in pairs:
+            runs = [(r + 1) * p // s - r * p // s for r in range(s)]
+            costs += [run + 2 for run in runs]
+        costs = sorted(costs * (B * H), reverse=True)
+        if len(costs) > 200000:
+            break
+        loads = [0.0] * min(n_cus, len(costs))
+        heapq.heapify(loads)
+        for c in costs:
+            heapq.heapreplace(loads, loads[0] + c)
+        us = max(loads) * _INTERVAL_US[D]
+        if s > 1:
+            rows = B * H * S
+            nbytes = 2 * s * rows * (D + 1) * 4 + rows * (D * 2 + 4)
+            us += nbytes / (_COMBINE_GBS * 1e3) + _COMBINE_FIXED_US
+        if us < best_us:
+            best, best_us = s, us
+    return best
+
+
+def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                n_splits: Union[int, str] = "auto", scale: Optional[float] = None,
+                causal: bool = False, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV attention forward: each query tile's keys are cut into
+    ``n_splits`` runs folded by separate workgroups, then merged by a combine
+    kernel. Same arguments and results as :func:`fwd`, plus ``n_splits``
+    ("auto" = :func:`choose_splits`) and an optional uint8 ``workspace`` of at
+    least ``splitkv_workspace_size`` bytes (allocated here when omitted).
+    """
+    B, H, S, D, scale, out, lse, stream = _prepare(q, k, v, scale, out, lse, stream)
+    if n_splits == "auto":
+        n_splits = choose_splits(B, H, S, D, bool(causal),
+                                 torch.cuda.get_device_properties(q.device).multi_processor_count)
+    n_splits = int(n_splits)
+    need = _lib.splitkv_workspace_size(B, H, S, D, n_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous CUDA tensor on q's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = _lib.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, H, S, D, scale, int(bool(causal)),
+                                   n_splits, ws_ptr, ws_bytes, stream.cuda_stream)
     _lib.check(st)
     return out, lse

@@ -479,11 +479,17 @@ __device__ __forceinline__ void softmax_any(Carrier<D> (&cr)[QSUB],
 // wave's previous tile, Q.K^T of its next one) followed by the softmax of the
 // tile just scored. K and V reach LDS by direct copies one interval ahead of
 // use.
-template <int D, bool CAUSAL>
+//
+// SPLIT: the key range of each query tile is cut into n_splits runs of whole
+// tile pairs (split-KV). Workgroup (query tile, head, split) folds its run
+// and stores the partial result -- o/d in fp32 and m + log2(d) -- into the
+// workspace instead of O and LSE; attn_combine_kernel merges the runs.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
-    int BH, int S, int n_qtiles, float c, uint32_t qsign) {
+    int BH, int S, int n_qtiles, int n_splits, float c, uint32_t qsign,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
   using G = Geometry<D>;
   constexpr int R = G::RING;
   __shared__ __attribute__((aligned(16))) _Float16 smem[G::LDS_HALVES];
@@ -499,7 +505,8 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   const int qgrp = wave % QGROUPS;
   const int parity = wave / QGROUPS;
 
-  const int bid = blockIdx.x;
+  const int split = SPLIT ? (int)(blockIdx.x % (unsigned)n_splits) : 0;
+  const int bid = SPLIT ? (int)(blockIdx.x / (unsigned)n_splits) : (int)blockIdx.x;
   const int qt = n_qtiles - 1 - bid / BH;
   const int bh = bid % BH;
   const int64_t head = (int64_t)bh * S * D;
@@ -558,30 +565,36 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
 
   const int kend = CAUSAL ? min(S, q0 + BLOCK_M) : S;
   const int n_kt = (kend + G::BN - 1) / G::BN;
-  const int n_pairs = (n_kt + 1) / 2;
+  const int n_pairs_all = (n_kt + 1) / 2;
+  // This workgroup folds tile pairs [pb, pb + n_pairs): all of them, or its
+  // split's run.
+  const int pb = SPLIT ? (int)((int64_t)split * n_pairs_all / n_splits) : 0;
+  const int n_pairs = SPLIT ? (int)((int64_t)(split + 1) * n_pairs_all / n_splits) - pb : n_pairs_all;
   // Pairs whose tile of this wave's parity holds keys for its rows: a prefix,
   // since tiles past S or past the wave's last query (causal) are skipped.
   const int row_end = CAUSAL ? min(kend, qrow0 + 32) : kend;  // keys < row_end are needed
   const int live_tiles = (row_end + G::BN - 1) / G::BN;
-  const int n_live = (live_tiles - parity + 1) / 2;
+  const int n_live = min(max((live_tiles - parity + 1) / 2 - pb, 0), n_pairs);
   // Only the last live pair of a wave can need element masks: the sequence
   // tail is in the last tile, and a tile crossing the causal diagonal of the
-  // wave's 32 rows is the last one at or below them.
+  // wave's 32 rows is the last one at or below them. (The last live pair of
+  // a split run is checked at run time.)
 
   CopyPlan<D> cp;
   make_copy_plan<D>(cp, wave, lane);
-  copy_pair<D>(cp.k_off, kh, 0, S, kring, wave);  // K of pair 0
+  if (n_pairs > 0) copy_pair<D>(cp.k_off, kh, 2 * pb * G::BN, S, kring, wave);  // K of pair pb
   wait_copies<0>();
   __syncthreads();
 
-  // Barrier interval j: P.V of pair j-1 and Q.K^T of pair j (MFMA), then the
-  // copies of K of pair j+1 and V of pair j, then the softmax of pair j
-  // (VALU); the probabilities stay in registers for interval j+1. The copies
-  // sit between the MFMA phase (whose LDS reads they would slow) and the
-  // softmax (which does not touch LDS). K of pair j is read from ring slot
-  // j % 2 and V of pair j-1 from slot (j-1) % 2, both copied in interval
-  // j-1. Every wave runs all n_pairs + 1 intervals; the body is specialised
-  // (compile-time flags) so that the steady state has no branches.
+  // Barrier interval j (pairs counted from pb): P.V of pair j-1 and Q.K^T of
+  // pair j (MFMA), then the copies of K of pair j+1 and V of pair j, then the
+  // softmax of pair j (VALU); the probabilities stay in registers for
+  // interval j+1. The copies sit between the MFMA phase (whose LDS reads they
+  // would slow) and the softmax (which does not touch LDS). K of pair j is
+  // read from ring slot j % 2 and V of pair j-1 from slot (j-1) % 2, both
+  // copied in interval j-1. Every wave runs all n_pairs + 1 intervals; the
+  // body is specialised (compile-time flags) so that the steady state has no
+  // branches.
   auto interval = [&](int j, auto pv_flag, auto qk_flag, auto edge_flag) {
     constexpr bool PV = decltype(pv_flag)::value;
     constexpr bool QK = decltype(qk_flag)::value;
@@ -591,12 +604,13 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     if constexpr (PV || QK) mfma_phase<D, PV, QK>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
     __builtin_amdgcn_sched_barrier(0);
     if (j + 1 < n_pairs)
-      copy_pair<D>(cp.k_off, kh, 2 * (j + 1) * G::BN, S, kring + ((j + 1) & 1) * G::SLOT_HALVES, wave);
+      copy_pair<D>(cp.k_off, kh, 2 * (pb + j + 1) * G::BN, S,
+                   kring + ((j + 1) & 1) * G::SLOT_HALVES, wave);
     if (j < n_pairs)
-      copy_pair<D>(cp.v_off, vh, 2 * j * G::BN, S, vring + (j & 1) * G::SLOT_HALVES, wave);
+      copy_pair<D>(cp.v_off, vh, 2 * (pb + j) * G::BN, S, vring + (j & 1) * G::SLOT_HALVES, wave);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (QK) {
-      const int key0 = (2 * j + parity) * G::BN;
+      const int key0 = (2 * (pb + j) + parity) * G::BN;
       if constexpr (EDGE)
         softmax_any<D, CAUSAL>(cr, sc, pf, c, key0, qrow0, S, li, g);
       else
@@ -637,6 +651,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
 
   float* lse_h = lse + (int64_t)bh * S;
   _Float16* oh = o + head;
+  const int64_t part_row0 = ((int64_t)split * BH + bh) * S;  // SPLIT: workspace rows
 #pragma unroll
   for (int qs = 0; qs < QSUB; ++qs) {
     const float* x = xfer + qs * (2 + 4 * G::D_BLOCKS) * 64;
@@ -645,8 +660,26 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const float w1 = __builtin_amdgcn_exp2f(cr[qs].m - m);
     const float w2 = __builtin_amdgcn_exp2f(m2 - m);
     const float dsum = group_sum(cr[qs].d * w1 + x[64] * w2);
-    const float inv = 1.0f / dsum;
     const int row = qrow0 + 16 * qs + li;
+    if constexpr (SPLIT) {
+      // A run can hold no visible key for a row (empty run, or causal keys
+      // above the row): its partial is o = 0 with weight 2^NEG_BIG = 0.
+      if (row < S) {
+        const bool empty = !(dsum > 0.0f);
+        const float inv = empty ? 0.0f : 1.0f / dsum;
+        float* po = part_o + (part_row0 + row) * D;
+#pragma unroll
+        for (int db = 0; db < G::D_BLOCKS; ++db) {
+          f32x4 val;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) val[r] = (cr[qs].o[db][r] * w1 + x[(2 + 4 * db + r) * 64] * w2) * inv;
+          *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g) = val;
+        }
+        if (g == 0) part_lse[part_row0 + row] = empty ? NEG_BIG : m + log2f(dsum);
+      }
+      continue;
+    }
+    const float inv = 1.0f / dsum;
     if (row < S) {
 #pragma unroll
       for (int db = 0; db < G::D_BLOCKS; ++db) {
@@ -659,6 +692,40 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       if (g == 0) lse_h[row] = (m + log2f(dsum)) * 0.69314718055994530942f;
     }
   }
+}
+
+// Merge of the split-KV partial results (the carrier merge law, with each
+// run's state given as o_s = o/d and l_s = m + log2 d): for every row,
+// M = max_s l_s, w_s = 2^(l_s - M), O = sum_s w_s o_s / sum_s w_s and
+// LSE = (M + log2 sum_s w_s) ln 2. One thread per row and 4 columns; reads and
+// writes are contiguous along the row (HBM-bound).
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_lse,
+                                                           _Float16* __restrict__ o,
+                                                           float* __restrict__ lse, int64_t rows,
+                                                           int n_splits) {
+  constexpr int TPR = D / 4;  // threads per row
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / TPR;
+  const int c4 = (int)(t % TPR);
+  if (row >= rows) return;
+  float M = NEG_BIG;
+  for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, part_lse[s * rows + row]);
+  float W = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < n_splits; ++s) {
+    const float w = __builtin_amdgcn_exp2f(part_lse[s * rows + row] - M);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + (s * rows + row) * D + 4 * c4);
+    W += w;
+    acc += w * v;
+  }
+  const float inv = 1.0f / W;
+  f16x4 h;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) h[r] = (_Float16)(acc[r] * inv);
+  *reinterpret_cast<f16x4*>(o + row * D + 4 * c4) = h;
+  if (c4 == 0) lse[row] = (M + log2f(W)) * 0.69314718055994530942f;
 }
 
 }  // namespace attn

@@ -33,11 +33,16 @@
 #ifndef ATTN_FWD_H
 #define ATTN_FWD_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 1
+#define ATTN_FWD_ABI_VERSION 2
+
+/* Largest n_splits accepted by attn_fwd_splitkv. */
+#define ATTN_MAX_SPLITS 64
 
 typedef enum {
   ATTN_OK = 0,
@@ -77,6 +82,41 @@ typedef enum {
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int S, int D, float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_splitkv -- the same operation with each query tile's keys cut into
+ * n_splits runs (split-KV), folded by separate workgroups and merged by a
+ * second kernel: more workgroups where B*H*ceil(S/128) leaves the GPU idle,
+ * and shorter critical paths for the long query tiles of a causal mask. The
+ * pages name this pairing of a split reduction with a combine kernel ("Learning
+ * FlashAttention the Hard Way, Part 2": The Move Stack, its REDUCE knob, and
+ * the Flash-Decoding reference, split-KV as split-K of the (m, d, o)
+ * carrier), and the merge is the carrier's associative combine.
+ *
+ *  q ... causal : as attn_fwd (same layouts, same checks, same status codes).
+ *  n_splits     : 1 .. ATTN_MAX_SPLITS. Each query tile's key range, in whole
+ *                 pairs of 64-key tiles, is cut into n_splits near-equal runs;
+ *                 runs may be empty. n_splits = 1 is exactly attn_fwd (the
+ *                 workspace is then not used and may be NULL).
+ *  workspace    : device buffer of at least workspace_size bytes, 16-byte
+ *                 aligned, owned by the caller; its contents on entry do not
+ *                 matter and are overwritten (per run and row: o/d in fp32 and
+ *                 m + log2 d in fp32). It must not alias any other argument,
+ *                 and two calls in flight must not share it.
+ *  workspace_size : its size in bytes, >= attn_fwd_splitkv_workspace_size().
+ *
+ *  Returns ATTN_OK once both kernels are enqueued on `stream`; ATTN_ERR_ARG
+ *  for n_splits out of range or a short workspace, ATTN_ERR_NULL for a NULL
+ *  workspace with n_splits > 1, ATTN_ERR_ALIGN for a misaligned one. Results
+ *  agree with attn_fwd to rounding, not bitwise.
+ */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int S, int D, float scale, int causal, int n_splits,
+                     void* workspace, size_t workspace_size, void* stream);
+
+/* Workspace bytes attn_fwd_splitkv needs: n_splits * B * H * S * (D + 1) * 4
+ * for n_splits > 1; 0 when n_splits == 1 or an argument is out of range. */
+size_t attn_fwd_splitkv_workspace_size(int B, int H, int S, int D, int n_splits);
 
 /* Static English name of a status code ("ATTN_OK", ...); never NULL. */
 const char* attn_status_string(int status);

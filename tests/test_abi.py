@@ -35,7 +35,8 @@ def declared_functions():
 def test_headers_exist_and_declare_entry_points():
     assert HEADERS
     names = declared_functions()
-    assert {"attn_fwd", "attn_status_string", "attn_last_error", "attn_version"} <= set(names)
+    assert {"attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_size",
+            "attn_status_string", "attn_last_error", "attn_version"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -97,6 +98,47 @@ def test_invalid_arguments_are_rejected_on_host(name, kw, status):
     assert msg, "an error must leave a message"
     with pytest.raises(_lib.AttnError, match=status):
         _lib.check(rc)
+
+
+W = A + 0x500000  # fake workspace address
+
+
+def _split(n_splits=2, ws=W, ws_bytes=1 << 30, **kw):
+    a = dict(q=A, k=B_, v=C, o=O, lse=L, B=1, H=2, S=128, D=64, scale=0.125, causal=0)
+    a.update(kw)
+    return _lib.attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"],
+                                 a["D"], a["scale"], a["causal"], n_splits, ws, ws_bytes, 0)
+
+
+SPLIT_INVALID = [
+    ("null q", dict(q=0), "ATTN_ERR_NULL"),
+    ("D=96", dict(D=96), "ATTN_ERR_UNSUPPORTED"),
+    ("lse misaligned", dict(lse=L + 2), "ATTN_ERR_ALIGN"),
+    ("causal=2", dict(causal=2), "ATTN_ERR_ARG"),
+    ("n_splits=0", dict(n_splits=0), "ATTN_ERR_ARG"),
+    ("n_splits=65", dict(n_splits=65), "ATTN_ERR_ARG"),
+    ("n_splits=-1", dict(n_splits=-1), "ATTN_ERR_ARG"),
+    ("null workspace", dict(ws=0), "ATTN_ERR_NULL"),
+    ("misaligned workspace", dict(ws=W + 8), "ATTN_ERR_ALIGN"),
+    ("short workspace", dict(ws_bytes=2 * 2 * 128 * 65 * 4 - 1), "ATTN_ERR_ARG"),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", SPLIT_INVALID, ids=[c[0] for c in SPLIT_INVALID])
+def test_splitkv_invalid_arguments_are_rejected_on_host(name, kw, status):
+    rc = _split(**kw)
+    assert _lib.STATUS_NAMES[rc] == status
+    assert _lib.load().attn_last_error().decode()
+
+
+def test_splitkv_workspace_size():
+    ws = _lib.splitkv_workspace_size
+    assert ws(1, 8, 4096, 64, 2) == 2 * 8 * 4096 * 65 * 4
+    assert ws(2, 3, 300, 128, 7) == 7 * 6 * 300 * 129 * 4
+    assert ws(1, 8, 4096, 64, 1) == 0            # single pass: no workspace
+    for bad in [(0, 1, 1, 64, 2), (1, 1, 0, 64, 2), (1, 1, 8, 96, 2), (1, 1, 8, 64, 0),
+                (1, 1, 8, 64, 65)]:
+        assert ws(*bad) == 0
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
