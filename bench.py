@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the sequence-length sweep (4k/8k/16k, B1 H8 D64)")
+                    help="skip the sequence-length sweep (4k/8k/16k, B1 H8 D64) and the "
+                         "split-KV comparison")
     ap.add_argument("--sweep-steps", type=int, default=30,
                     help="timed launches per sweep point")
     return ap.parse_args()
@@ -177,6 +178,46 @@ def run_sweep(attn, dev, stream, steps):
     return out
 
 
+def run_splitkv(attn, dev, stream, steps):
+    """Single-pass vs split-KV (split count from the library's heuristic) on
+    workloads that leave CUs idle or unbalanced in one pass."""
+    import torch
+
+    from testkit import SPLITKV_BENCH, WORKLOADS, workload_inputs
+
+    out = []
+    for name in SPLITKV_BENCH:
+        w = WORKLOADS[name]
+        q, k, v = (torch.from_numpy(x).to(dev) for x in workload_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+        ns = attn.choose_splits(w.B, w.H, w.S, w.D, w.causal,
+                                torch.cuda.get_device_properties(dev).multi_processor_count)
+        ws = torch.empty(max(1, attn.splitkv_workspace_size(w.B, w.H, w.S, w.D, ns)),
+                         dtype=torch.uint8, device=dev)
+
+        def single():
+            attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+
+        def split():
+            attn.fwd_splitkv(q, k, v, n_splits=ns, scale=w.scale, causal=w.causal, out=o,
+                             lse=lse, workspace=ws, stream=stream)
+
+        rec = {"workload": name, "n_splits": ns}
+        for tag, fn in (("single_pass", single), ("splitkv", split)):
+            for _ in range(5):
+                fn()
+            durs, _ = time_launches(fn, stream, steps)
+            rec[f"{tag}_us_mean"] = round(float(durs.mean()) * 1e3, 3)
+            rec[f"{tag}_us_median"] = round(float(np.median(durs)) * 1e3, 3)
+            rec[f"{tag}_tflops"] = round(w.flops / (float(durs.mean()) * 1e-3) / 1e12, 2)
+        rec["speedup"] = round(rec["single_pass_us_mean"] / rec["splitkv_us_mean"], 3)
+        log(f"splitkv {name}: {rec}")
+        out.append(rec)
+        del q, k, v, o, lse, ws
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -264,6 +305,7 @@ def main():
     }
     if not args.no_sweep:
         result["sweep"] = run_sweep(attn, dev, stream, args.sweep_steps)
+        result["splitkv"] = run_splitkv(attn, dev, stream, args.sweep_steps)
     if not args.no_cpu_baseline:
         log("CPU oracle leg ...")
         o_np = o.cpu().numpy()

@@ -76,7 +76,13 @@ WORKLOADS = {
         "sweep_causal_b1h8s8192d64", 1, 8, 8192, 64, True, SEED_BASE + 8),
     "sweep_causal_b1h8s16384d64": Workload(
         "sweep_causal_b1h8s16384d64", 1, 8, 16384, 64, True, SEED_BASE + 9),
+    # One head: 128 query tiles leave half of 256 CUs idle in a single pass.
+    "single_head_b1h1s16384d64": Workload(
+        "single_head_b1h1s16384d64", 1, 1, 16384, 64, False, SEED_BASE + 10),
 }
+
+# Workloads on which the split-KV path is timed against the single pass.
+SPLITKV_BENCH = ("single_head_b1h1s16384d64", "sweep_causal_b1h8s4096d64")
 
 HEADLINE = "sdpa_b1h8s4096d64"
 

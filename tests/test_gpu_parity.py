@@ -74,7 +74,7 @@ def test_headline_workload_full_compare():
 @pytest.mark.parametrize("name", ["long_b1h8s16384d64", "causal_b2h16s8192d128",
                                   "peaked_causal_b4h32s4096d128", "sweep_b1h8s8192d64",
                                   "sweep_causal_b1h8s4096d64", "sweep_causal_b1h8s8192d64",
-                                  "sweep_causal_b1h8s16384d64"])
+                                  "sweep_causal_b1h8s16384d64", "single_head_b1h1s16384d64"])
 def test_large_workload_sampled_rows(name):
     w = WORKLOADS[name]
     _announce(name)

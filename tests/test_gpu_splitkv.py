@@ -80,6 +80,7 @@ def test_one_split_is_the_single_pass_path_bitwise():
 
 
 @pytest.mark.parametrize("name,n_splits", [("sweep_causal_b1h8s4096d64", "auto"),
+                                           ("single_head_b1h1s16384d64", "auto"),
                                            ("sdpa_b1h8s4096d64", 2),
                                            ("causal_b2h16s8192d128", 3)])
 def test_splitkv_workload_sampled_rows(name, n_splits):
