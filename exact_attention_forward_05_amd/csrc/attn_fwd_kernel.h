@@ -90,6 +90,12 @@ struct Geometry {
   // At D = 128 the Q fragments would not fit the register budget next to the
   // output accumulators: the workgroup's Q rows are staged in LDS instead.
   static constexpr bool Q_IN_LDS = D == 128;
+  // Odd waves run half an interval out of phase with even waves (softmax
+  // against the other wave's MFMA phase). Each 16x16x32 MFMA blocks the other
+  // wave's VALU issue for about half its 16 cycles, so this pays only where
+  // the MFMA phase is long next to the softmax: at D = 128 (5% on causal
+  // B2 H16 S8192), not at D = 64 (5% slower).
+  static constexpr bool PINGPONG = D == 128;
   static constexpr int Q_HALVES = Q_IN_LDS ? BLOCK_M * D : 0;
   static constexpr int LDS_HALVES = 2 * RING * SLOT_HALVES + Q_HALVES;
   static constexpr int LDS_BYTES = LDS_HALVES * 2;
@@ -477,8 +483,9 @@ __device__ __forceinline__ void softmax_any(Carrier<D> (&cr)[QSUB],
 // Schedule. Key tiles come in pairs (2p, 2p+1): even waves fold tile 2p and
 // odd waves tile 2p+1. Each barrier interval is an MFMA phase (P.V of the
 // wave's previous tile, Q.K^T of its next one) followed by the softmax of the
-// tile just scored. K and V reach LDS by direct copies one interval ahead of
-// use.
+// tile just scored; at D = 128 odd waves take the two halves in the other
+// order (softmax of the tile scored in the previous interval first). K and V
+// reach LDS by direct copies one interval ahead of use.
 //
 // SPLIT: the key range of each query tile is cut into n_splits runs of whole
 // tile pairs (split-KV). Workgroup (query tile, head, split) folds its run
@@ -575,6 +582,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   const int row_end = CAUSAL ? min(kend, qrow0 + 32) : kend;  // keys < row_end are needed
   const int live_tiles = (row_end + G::BN - 1) / G::BN;
   const int n_live = min(max((live_tiles - parity + 1) / 2 - pb, 0), n_pairs);
+  constexpr bool PINGPONG = G::PINGPONG;
   // Only the last live pair of a wave can need element masks: the sequence
   // tail is in the last tile, and a tile crossing the causal diagonal of the
   // wave's 32 rows is the last one at or below them. (The last live pair of
@@ -595,42 +603,75 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   // copied in interval j-1. Every wave runs all n_pairs + 1 intervals; the
   // body is specialised (compile-time flags) so that the steady state has no
   // branches.
-  auto interval = [&](int j, auto pv_flag, auto qk_flag, auto edge_flag) {
-    constexpr bool PV = decltype(pv_flag)::value;
-    constexpr bool QK = decltype(qk_flag)::value;
-    constexpr bool EDGE = decltype(edge_flag)::value;  // the tile may need masks
-    const _Float16* kslot = kring + (j & 1) * G::SLOT_HALVES + parity * G::K_HALVES;
-    const _Float16* vslot = vring + ((j + 1) & 1) * G::SLOT_HALVES + parity * G::V_HALVES;
-    if constexpr (PV || QK) mfma_phase<D, PV, QK>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
-    __builtin_amdgcn_sched_barrier(0);
+  auto copies = [&](int j) __attribute__((always_inline)) {
     if (j + 1 < n_pairs)
       copy_pair<D>(cp.k_off, kh, 2 * (pb + j + 1) * G::BN, S,
                    kring + ((j + 1) & 1) * G::SLOT_HALVES, wave);
     if (j < n_pairs)
       copy_pair<D>(cp.v_off, vh, 2 * (pb + j) * G::BN, S, vring + (j & 1) * G::SLOT_HALVES, wave);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (QK) {
-      const int key0 = (2 * (pb + j) + parity) * G::BN;
-      if constexpr (EDGE)
-        softmax_any<D, CAUSAL>(cr, sc, pf, c, key0, qrow0, S, li, g);
-      else
-        softmax_tile<D, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
-    }
+  };
+  // softmax of pair p of this wave's parity (masks possible when EDGE)
+  auto softmax_pair = [&](int p, auto edge_flag) __attribute__((always_inline)) {
+    const int key0 = (2 * (pb + p) + parity) * G::BN;
+    if constexpr (decltype(edge_flag)::value)
+      softmax_any<D, CAUSAL>(cr, sc, pf, c, key0, qrow0, S, li, g);
+    else
+      softmax_tile<D, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
+  };
+  auto mfma = [&](int j, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_flag)::value;
+    constexpr bool QK = decltype(qk_flag)::value;
+    const _Float16* kslot = kring + (j & 1) * G::SLOT_HALVES + parity * G::K_HALVES;
+    const _Float16* vslot = vring + ((j + 1) & 1) * G::SLOT_HALVES + parity * G::V_HALVES;
+    if constexpr (PV || QK) mfma_phase<D, PV, QK>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+  };
+  auto end_interval = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     wait_copies<0>();
     __syncthreads();
   };
+  // Even waves: MFMA phase, copies, softmax of the pair just scored.
+  auto even_interval = [&](int j, auto pv_flag, auto qk_flag, auto edge_flag) __attribute__((always_inline)) {
+    mfma(j, pv_flag, qk_flag);
+    __builtin_amdgcn_sched_barrier(0);
+    copies(j);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(qk_flag)::value) softmax_pair(j, edge_flag);
+    end_interval();
+  };
+  // Odd waves run the same work half an interval out of phase: the softmax of
+  // the pair scored in the previous interval, copies, then the MFMA phase. On
+  // each SIMD one wave's softmax thus overlaps the other's MFMA phase.
+  auto odd_interval = [&](int j, auto sm_flag, auto edge_flag, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
+    if constexpr (decltype(sm_flag)::value) softmax_pair(j - 1, edge_flag);
+    __builtin_amdgcn_sched_barrier(0);
+    copies(j);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(j, pv_flag, qk_flag);
+    end_interval();
+  };
   using T_ = std::true_type;
   using F_ = std::false_type;
   int j = 0;
-  if (n_live >= 1)
-    interval(j++, F_{}, T_{}, T_{});
-  else
-    interval(j++, F_{}, F_{}, F_{});
-  for (; j + 1 < n_live; ++j) interval(j, T_{}, T_{}, F_{});  // steady state
-  if (j + 1 == n_live) interval(j++, T_{}, T_{}, T_{});       // last live pair
-  if (j == n_live && j >= 1) interval(j++, T_{}, F_{}, F_{}); // its P.V
-  for (; j <= n_pairs; ++j) interval(j, F_{}, F_{}, F_{});    // idle: copies and barriers
+  if (parity == 0 || !PINGPONG) {
+    if (n_live >= 1)
+      even_interval(j++, F_{}, T_{}, T_{});
+    else
+      even_interval(j++, F_{}, F_{}, F_{});
+    for (; j + 1 < n_live; ++j) even_interval(j, T_{}, T_{}, F_{});  // steady state
+    if (j + 1 == n_live) even_interval(j++, T_{}, T_{}, T_{});       // last live pair
+    if (j == n_live && j >= 1) even_interval(j++, T_{}, F_{}, F_{}); // its P.V
+    for (; j <= n_pairs; ++j) even_interval(j, F_{}, F_{}, F_{});    // idle: copies, barriers
+  } else {
+    // flags: softmax of the previous pair, its masks, P.V, Q.K^T
+    if (n_live >= 1)
+      odd_interval(j++, F_{}, F_{}, F_{}, T_{});
+    else
+      odd_interval(j++, F_{}, F_{}, F_{}, F_{});
+    for (; j < n_live; ++j) odd_interval(j, T_{}, F_{}, T_{}, T_{});   // steady state
+    if (j == n_live && j >= 1) odd_interval(j++, T_{}, T_{}, T_{}, F_{}); // last live pair
+    for (; j <= n_pairs; ++j) odd_interval(j, F_{}, F_{}, F_{}, F_{});  // idle
+  }
 
   // Odd-tile waves hand their carriers to their even-tile partners.
   float* xfer = reinterpret_cast<float*>(smem) + qgrp * 64 * G::CARRIER_FLOATS + lane;
