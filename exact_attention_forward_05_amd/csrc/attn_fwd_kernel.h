@@ -96,6 +96,11 @@ struct Geometry {
   // the MFMA phase is long next to the softmax: at D = 128 (5% on causal
   // B2 H16 S8192), not at D = 64 (5% slower).
   static constexpr bool PINGPONG = D == 128;
+  // At D = 64 a tile's P.V runs in the same interval as its Q.K^T and
+  // softmax (three phases, V copied one interval earlier): the SIMD's two
+  // waves then interleave shorter MFMA phases with their softmaxes (1-3%
+  // faster). At D = 128 the ping-pong order measured faster than this.
+  static constexpr bool PV_SAME = D == 64;
   // A wave in its softmax raises its issue priority (s_setprio), so that the
   // SIMD's other wave, in its MFMA phase or later in its own softmax, does not
   // starve it (2-3% on every workload).
@@ -485,11 +490,13 @@ __device__ __forceinline__ void softmax_any(Carrier<D> (&cr)[QSUB],
 // consecutive workgroups take consecutive heads.
 //
 // Schedule. Key tiles come in pairs (2p, 2p+1): even waves fold tile 2p and
-// odd waves tile 2p+1. Each barrier interval is an MFMA phase (P.V of the
-// wave's previous tile, Q.K^T of its next one) followed by the softmax of the
-// tile just scored; at D = 128 odd waves take the two halves in the other
-// order (softmax of the tile scored in the previous interval first). K and V
-// reach LDS by direct copies one interval ahead of use.
+// odd waves tile 2p+1, one pair per barrier interval, with K and V copied
+// into LDS during the interval before they are read.
+//  D = 64: interval j is Q.K^T of pair j, the softmax, then P.V of pair j.
+//  D = 128: interval j is an MFMA phase (P.V of pair j-1, Q.K^T of pair j)
+//    and the softmax of pair j; odd waves take the two halves in the other
+//    order (softmax of pair j-1 first), so that on each SIMD one wave's
+//    softmax runs against the other's MFMA phase.
 //
 // SPLIT: the key range of each query tile is cut into n_splits runs of whole
 // tile pairs (split-KV). Workgroup (query tile, head, split) folds its run
@@ -568,9 +575,9 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
 #pragma unroll
     for (int db = 0; db < G::D_BLOCKS; ++db) cr[qs].o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // fp16 probabilities of the wave's last scored tile, carried across the
-  // barrier into the next interval's P.V; sc holds a tile's scores between
-  // Q.K^T and softmax within one interval.
+  // sc: a tile's scores between Q.K^T and softmax; pf: its fp16
+  // probabilities between softmax and P.V (at D = 128 carried across the
+  // barrier into the next interval).
   f16x8 pf[QSUB][G::KC];
   f32x4 sc[QSUB][G::KB];
 
@@ -595,18 +602,21 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   CopyPlan<D> cp;
   make_copy_plan<D>(cp, wave, lane);
   if (n_pairs > 0) copy_pair<D>(cp.k_off, kh, 2 * pb * G::BN, S, kring, wave);  // K of pair pb
+  if constexpr (G::PV_SAME) {
+    if (n_pairs > 0) copy_pair<D>(cp.v_off, vh, 2 * pb * G::BN, S, vring, wave);  // V of pair pb
+  }
   wait_copies<0>();
   __syncthreads();
 
-  // Barrier interval j (pairs counted from pb): P.V of pair j-1 and Q.K^T of
-  // pair j (MFMA), then the copies of K of pair j+1 and V of pair j, then the
-  // softmax of pair j (VALU); the probabilities stay in registers for
-  // interval j+1. The copies sit between the MFMA phase (whose LDS reads they
-  // would slow) and the softmax (which does not touch LDS). K of pair j is
-  // read from ring slot j % 2 and V of pair j-1 from slot (j-1) % 2, both
-  // copied in interval j-1. Every wave runs all n_pairs + 1 intervals; the
-  // body is specialised (compile-time flags) so that the steady state has no
-  // branches.
+  // Two-phase order (D = 128), barrier interval j (pairs counted from pb):
+  // P.V of pair j-1 and Q.K^T of pair j (MFMA), then the copies of K of pair
+  // j+1 and V of pair j, then the softmax of pair j (VALU); the
+  // probabilities stay in registers for interval j+1. The copies sit between
+  // the MFMA phase (whose LDS reads they would slow) and the softmax (which
+  // does not touch LDS). K of pair j is read from ring slot j % 2 and V of
+  // pair j-1 from slot (j-1) % 2, both copied in interval j-1. Every wave
+  // runs all n_pairs + 1 intervals; the bodies are specialised (compile-time
+  // flags) so that the steady state has no branches.
   auto copies = [&](int j) __attribute__((always_inline)) {
     if (j + 1 < n_pairs)
       copy_pair<D>(cp.k_off, kh, 2 * (pb + j + 1) * G::BN, S,
@@ -659,7 +669,37 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   using T_ = std::true_type;
   using F_ = std::false_type;
   int j = 0;
-  if (parity == 0 || !PINGPONG) {
+  if constexpr (G::PV_SAME) {
+    // Three-phase order (D = 64), interval j: Q.K^T of pair j, copies of K
+    // and V of pair j+1 (into the slots of pair j-1, read in interval j-1),
+    // softmax of pair j, P.V of pair j. Every wave runs n_pairs intervals.
+    auto copies_next = [&](int jj) __attribute__((always_inline)) {
+      if (jj + 1 < n_pairs) {
+        copy_pair<D>(cp.k_off, kh, 2 * (pb + jj + 1) * G::BN, S,
+                     kring + ((jj + 1) & 1) * G::SLOT_HALVES, wave);
+        copy_pair<D>(cp.v_off, vh, 2 * (pb + jj + 1) * G::BN, S,
+                     vring + ((jj + 1) & 1) * G::SLOT_HALVES, wave);
+      }
+    };
+    auto full = [&](int jj, auto edge_flag) __attribute__((always_inline)) {
+      const _Float16* kslot = kring + (jj & 1) * G::SLOT_HALVES + parity * G::K_HALVES;
+      const _Float16* vslot = vring + (jj & 1) * G::SLOT_HALVES + parity * G::V_HALVES;
+      mfma_phase<D, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+      __builtin_amdgcn_sched_barrier(0);
+      copies_next(jj);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_pair(jj, edge_flag);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_phase<D, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+      end_interval();
+    };
+    for (; j + 1 < n_live; ++j) full(j, F_{});
+    if (j + 1 == n_live) full(j++, T_{});
+    for (; j < n_pairs; ++j) {
+      copies_next(j);
+      end_interval();
+    }
+  } else if (parity == 0 || !PINGPONG) {
     if (n_live >= 1)
       even_interval(j++, F_{}, T_{}, T_{});
     else
