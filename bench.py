@@ -23,6 +23,10 @@ import numpy as np
 # Published MI355X dense peaks / bandwidth (no sparsity).
 PEAK_FP16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+# Exponential throughput used for the secondary (transcendental) bound: one
+# v_exp_f32 per visible score; a wave64 v_exp_f32 issues every 9 cycles per
+# SIMD (measured), 1024 SIMDs, at the 2.4 GHz peak clock.
+EXP_PER_S = 1024 * 64 / 9.0 * 2.4e9
 METRIC = "attn fwd TFLOP/s & µs, fp16 B1 H8 S4096 D64; % of dense FP16 MFMA peak"
 
 
@@ -84,6 +88,23 @@ def profiled_traffic(workload: str):
     return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def visible_scores(w) -> int:
+    """Score elements the method exponentiates: S^2 per head, or S(S+1)/2 causal."""
+    per_head = w.S * (w.S + 1) // 2 if w.causal else w.S * w.S
+    return w.B * w.H * per_head
+
+
 def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, sample_rows: int):
     """Time the fp64 oracle on the host over a bounded sample of the workload and
     compare the GPU output with it on that sample."""
@@ -124,7 +145,8 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, sample_rows: int):
               "pass": bool(err.max() <= 4e-3 and err.mean() <= 5e-4
                            and np.abs(lg.astype(np.float64) - L).max() <= 1e-3)}
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": blas_threads,
-            "kind": "oracle", "sample": desc, "seconds": secs,
+            "kind": "oracle", "sample": desc, "seconds": secs, "cpu_model": cpu_model(),
+            "host_threads": os.cpu_count(),
             "note": "fp64 numpy oracle; matmuls on BLAS threads, exp/max/sum single-threaded"}, parity
 
 
@@ -300,6 +322,12 @@ def main():
                      "kernel": f"attn_fwd_kernel<{w.D},{str(w.causal).lower()}>",
                      "algorithmic_flops_per_launch": w.flops,
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
+        # secondary bounds at the same launch time: exponentials and HBM
+        "exp_bound": {"exps_per_launch": visible_scores(w),
+                      "us_at_exp_peak": round(visible_scores(w) / EXP_PER_S * 1e6, 3),
+                      "frac": round(visible_scores(w) / EXP_PER_S / (avg_ms * 1e-3), 4)},
+        "hbm_bound": {"us_at_hbm_peak": round(w.algorithmic_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 3),
+                      "frac": round(w.algorithmic_bytes / (avg_ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }
