@@ -9,13 +9,14 @@
 // translated from the page's mma.sync listings.
 //
 // Work decomposition. A workgroup of 8 waves owns BLOCK_M = 128 query rows of
-// one (batch, head). Waves 0-3 take 32 rows each and fold the even key tiles
-// (64 or 128 keys); waves 4-7 take the same rows and fold the odd tiles.
-// The two waves on one SIMD therefore work on independent data, so the MFMA
-// work of one overlaps the softmax VALU work of the other (a single wave
-// serialises its own MFMA and VALU instructions on gfx950). At the end each
-// odd-tile wave hands its carrier to its partner through LDS and the two are
-// merged.
+// one (batch, head). Waves 0-3 take 32 rows each and fold the even 64-key
+// tiles; waves 4-7 take the same rows and fold the odd tiles. The two waves on
+// one SIMD therefore work on independent data and can fill each other's
+// stalls (a single wave serialises its own MFMA and VALU instructions on
+// gfx950, and a softmax barely progresses while the other wave streams
+// MFMAs, so the interval order is chosen per head dimension; see the schedule
+// note at the kernel). At the end each odd-tile wave hands its carrier to its
+// partner through LDS and the two are merged.
 //
 // MFMA: v_mfma_f32_16x16x32_f16. Lane l = 16*g + i (g = 0..3, i = 0..15):
 //   A: row i, contraction slots (g, 0..7); B: column i, slots (g, 0..7);
@@ -42,7 +43,7 @@
 // (v_dot2), so d normalises exactly the weights the P.V product used.
 //
 // LDS. K and V tiles arrive by direct global->LDS loads into two-slot rings
-// of tile pairs, V one barrier interval behind K. K rows are stored in
+// of tile pairs, one barrier interval before they are read. K rows are stored in
 // MFMA-row order (row 16*kb + i holds key st_key(kb, i)), V rows in key order;
 // both are unpadded with XOR-permuted 16-byte chunks so that every operand
 // read is free of bank conflicts on the 64-bank LDS. V^T operands come from
