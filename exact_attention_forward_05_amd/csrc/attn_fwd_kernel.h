@@ -230,16 +230,8 @@ __device__ __forceinline__ void copy_pair(const uint32_t* off, const _Float16* b
   }
 }
 
-// Wait until at most N direct copies (vector memory operations) of this wave
-// are still in flight.
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-  static_assert(N == 0 || N == 2 || N == 4 || N == 8, "unsupported count");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-}
+// Wait until this wave's direct copies (vector memory operations) are done.
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // LDS transposing read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane n supplies the address of 4 consecutive halves X[n][0..3]; lane n
@@ -606,7 +598,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   if constexpr (G::PV_SAME) {
     if (n_pairs > 0) copy_pair<D>(cp.v_off, vh, 2 * pb * G::BN, S, vring, wave);  // V of pair pb
   }
-  wait_copies<0>();
+  wait_copies();
   __syncthreads();
 
   // Two-phase order (D = 128), barrier interval j (pairs counted from pb):
@@ -644,7 +636,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   };
   auto end_interval = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    wait_copies<0>();
+    wait_copies();
     __syncthreads();
   };
   // Even waves: MFMA phase, copies, softmax of the pair just scored.
