@@ -1,0 +1,68 @@
+"""Host logic of bench.py, without a GPU: the one-GPU contract, the kernel
+source hash that ties a profile summary to the kernel, the profile lookup,
+and the work counts the roofline divides by."""
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from testkit import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    csrc = tmp_path / "exact_attention_forward_05_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in bench.KERNEL_SOURCES:
+        shutil.copy(os.path.join(ROOT, "exact_attention_forward_05_amd", "csrc", f), csrc / f)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    k = csrc / bench.KERNEL_SOURCES[0]
+    text = k.read_text()
+    k.write_text("// an added comment\n/* and a block\n comment */\n" + text.replace("\n", "\n\n", 3))
+    assert bench.kernel_source_hash() == h0
+    k.write_text(text.replace("P_LIMIT = 16384.0f", "P_LIMIT = 8192.0f", 1))
+    assert bench.kernel_source_hash() != h0
+
+
+def test_profiled_traffic_lookup(tmp_path, monkeypatch):
+    """A summary's traffic is used only for its workload and only while its
+    source hash is the current one."""
+    csrc = tmp_path / "exact_attention_forward_05_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in bench.KERNEL_SOURCES:
+        shutil.copy(os.path.join(ROOT, "exact_attention_forward_05_amd", "csrc", f), csrc / f)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h = bench.kernel_source_hash()
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    rec = {"workload": "sdpa_b1h8s4096d64", "source_hash": h, "traffic_bytes_per_launch": 123}
+    old = dict(rec, workload="long_b1h8s16384d64", source_hash="0" * 16)
+    (prof / "a.md").write_text("text\n```json\n" + json.dumps(rec) + "\n```\n")
+    (prof / "b.md").write_text("```json\n" + json.dumps(old) + "\n```\n")
+    assert bench.profiled_traffic("sdpa_b1h8s4096d64") == 123
+    assert bench.profiled_traffic("long_b1h8s16384d64") is None   # stale hash
+    assert bench.profiled_traffic("no_such_workload") is None
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_work_counts(name):
+    w = WORKLOADS[name]
+    per_head = w.S * (w.S + 1) // 2 if w.causal else w.S * w.S
+    assert bench.visible_scores(w) == w.B * w.H * per_head
+    full = 4.0 * w.B * w.H * w.S * w.S * w.D
+    assert w.flops == (full / 2 if w.causal else full)
+    assert w.algorithmic_bytes == 8 * w.B * w.H * w.S * w.D + 4 * w.B * w.H * w.S
