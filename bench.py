@@ -47,6 +47,8 @@ def parse():
                          "split-KV comparison")
     ap.add_argument("--sweep-steps", type=int, default=30,
                     help="timed launches per sweep point")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time launches with caches flushed (512 MB written before each)")
     return ap.parse_args()
 
 
@@ -197,6 +199,29 @@ def time_launches(step, stream, steps):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return np.array([s.elapsed_time(e) / n for s, e, n in zip(starts, ends, sizes)]), wall
+
+
+def time_cold(step, dev, stream, steps):
+    """Per-launch time with the L2 and the infinity cache flushed: a 512 MB
+    buffer is written on the same stream before each launch, outside the
+    event pair around it."""
+    import torch
+
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    durs = []
+    for _ in range(steps):
+        scratch.fill_(1)
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        step()
+        s1.record(stream)
+        durs.append((s0, s1))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in durs])
+    del scratch
+    return {"us_mean": round(float(ms.mean()) * 1e3, 3),
+            "us_median": round(float(np.median(ms)) * 1e3, 3), "launches": steps}
 
 
 def run_sweep(attn, dev, stream, steps):
@@ -365,6 +390,9 @@ def main():
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }
+    if args.cold:
+        result["cold"] = time_cold(step, dev, stream, min(args.steps, 50))
+        log(f"cold launches: {result['cold']}")
     if not args.no_sweep:
         result["sweep"] = run_sweep(attn, dev, stream, args.sweep_steps)
         result["splitkv"] = run_splitkv(attn, dev, stream, args.sweep_steps)
