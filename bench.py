@@ -57,7 +57,7 @@ def log(msg):
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip")
+KERNEL_SOURCES = ("attn_fwd_kernel.h", "work_order.h", "attn_fwd.hip")
 
 
 def kernel_source_hash() -> str:

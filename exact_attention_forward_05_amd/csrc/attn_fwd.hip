@@ -36,13 +36,29 @@ int64_t workspace_bytes(int B, int H, int S, int D, int n_splits) {
   return part_o_bytes(B, H, S, D, n_splits) + (int64_t)n_splits * B * H * S * 4;
 }
 
+// Causal launches are folded (ORDER_FOLDED) from this many workgroups on:
+// the CU count of MI355X, one workgroup per CU.
+constexpr int64_t FOLD_MIN_WORKGROUPS = 256;
+
 template <int D, bool CAUSAL>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
            int S, float scale, int n_splits, void* workspace, hipStream_t stream) {
   using namespace attn;
   const int BH = B * H;
   const int n_qtiles = (S + BLOCK_M - 1) / BLOCK_M;
-  const int64_t blocks = (int64_t)BH * n_qtiles * n_splits;
+  // Single pass: non-causal work is uniform, so the order serves L2 locality
+  // alone (head-major per XCD). Causal tiles range from 1 to n_qtiles key
+  // tile pairs: folded mirror pairs equalise them when there are enough to
+  // fill the CUs, else the heaviest tiles go first.
+  int order = ORDER_TILES;
+  if (n_splits == 1) {
+    if (!CAUSAL)
+      order = ORDER_HEADS;
+    else if ((int64_t)BH * ((n_qtiles + 1) / 2) >= FOLD_MIN_WORKGROUPS)
+      order = ORDER_FOLDED;
+  }
+  const int64_t blocks = (int64_t)BH * (order == ORDER_FOLDED ? (n_qtiles + 1) / 2 : n_qtiles) *
+                         n_splits;
   if (blocks > 0x7fffffff) return fail(ATTN_ERR_SHAPE, "grid of %lld workgroups is too large",
                                        (long long)blocks);
   // Scores are folded in base 2: t = s * |scale| * log2(e). A negative scale
@@ -55,15 +71,15 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   _Float16* oh = static_cast<_Float16*>(o);
   if (n_splits == 1) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false>), dim3((unsigned)blocks), dim3(THREADS),
-                       0, stream, qh, kh, vh, oh, lse, BH, S, n_qtiles, 1, c, qsign, nullptr,
-                       nullptr);
+                       0, stream, qh, kh, vh, oh, lse, BH, S, n_qtiles, 1, order, c, qsign,
+                       nullptr, nullptr);
   } else {
     float* part_o = static_cast<float*>(workspace);
     float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                part_o_bytes(B, H, S, D, n_splits));
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, true>), dim3((unsigned)blocks), dim3(THREADS),
-                       0, stream, qh, kh, vh, oh, lse, BH, S, n_qtiles, n_splits, c, qsign,
-                       part_o, part_lse);
+                       0, stream, qh, kh, vh, oh, lse, BH, S, n_qtiles, n_splits, order, c,
+                       qsign, part_o, part_lse);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
       return fail(ATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));

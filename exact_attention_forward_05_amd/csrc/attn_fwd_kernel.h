@@ -55,6 +55,8 @@
 
 #include <type_traits>
 
+#include "work_order.h"
+
 namespace attn {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -478,9 +480,7 @@ __device__ __forceinline__ void softmax_any(Carrier<D> (&cr)[QSUB],
     softmax_tile<D, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
 }
 
-// grid.x = BH * n_qtiles; workgroup id -> (query tile, batch*head). The
-// heaviest (last) query tiles are issued first, which balances causal work;
-// consecutive workgroups take consecutive heads.
+// Workgroup id -> (batch*head, query tiles) by `order` (work_order.h).
 //
 // Schedule. Key tiles come in pairs (2p, 2p+1): even waves fold tile 2p and
 // odd waves tile 2p+1, one pair per barrier interval, with K and V copied
@@ -499,7 +499,7 @@ template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
-    int BH, int S, int n_qtiles, int n_splits, float c, uint32_t qsign,
+    int BH, int S, int n_qtiles, int n_splits, int order, float c, uint32_t qsign,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
   using G = Geometry<D>;
   constexpr int R = G::RING;
@@ -508,268 +508,284 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   _Float16* vring = smem + R * G::SLOT_HALVES;      // [slot][tile] V tiles
   _Float16* qtile = smem + 2 * R * G::SLOT_HALVES;  // Q rows of the workgroup (Q_IN_LDS)
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int li = lane & 15;
-  const int g = lane >> 4;
-  const int qgrp = wave % QGROUPS;
-  const int parity = wave / QGROUPS;
-
   const int split = SPLIT ? (int)(blockIdx.x % (unsigned)n_splits) : 0;
   const int bid = SPLIT ? (int)(blockIdx.x / (unsigned)n_splits) : (int)blockIdx.x;
-  const int qt = n_qtiles - 1 - bid / BH;
-  const int bh = bid % BH;
+  const TileWork work = work_of(SPLIT ? ORDER_TILES : order, bid, BH, n_qtiles);
+  const int bh = work.bh;
   const int64_t head = (int64_t)bh * S * D;
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, (uint32_t)S * D * 2);
   const _Float16* kh = k + head;
   const _Float16* vh = v + head;
 
-  const int q0 = qt * BLOCK_M;
-  const int qrow0 = q0 + 32 * qgrp;  // this wave's first query row
+  // One query tile: Q load, the key loop and the epilogue. Odd-tile waves
+  // leave it after handing over their carriers.
+  auto run_tile = [&](const int qt) __attribute__((always_inline)) {
+    // Lane indices are derived afresh for each tile (the empty asm hides
+    // the thread id from the optimiser), so that nothing lane-dependent is
+    // hoisted out of the tile loop and held in registers across the key loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int li = lane & 15;
+    const int g = lane >> 4;
+    const int qgrp = wave % QGROUPS;
+    const int parity = wave / QGROUPS;
+    const int q0 = qt * BLOCK_M;
+    const int qrow0 = q0 + 32 * qgrp;  // this wave's first query row
 
-  // Q^T fragments, loaded once (sign-flipped when the scale is negative):
-  // into registers, or (Q_IN_LDS) the workgroup's Q rows into LDS by direct
-  // copies, chunks permuted like K rows; rows past S read as zeros.
-  f16x8 qf[QSUB][G::D_CHUNKS];
-  if constexpr (G::Q_IN_LDS) {
-    constexpr int UNITS = BLOCK_M * D * 2 / 1024;  // 1 KB copy units
-    static_assert(UNITS % WAVES == 0, "Q copy split");
-#pragma unroll
-    for (int i = 0; i < UNITS / WAVES; ++i) {
-      const int unit = i * WAVES + wave;
-      const int slot = unit * 64 + lane;
-      const int row = slot / (D / 8);
-      const int pc = slot % (D / 8);
-      const uint32_t off = (uint32_t)(((q0 + row) * D + 8 * (pc ^ k_swizzle<D>(row))) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          qrs, (__attribute__((address_space(3))) void*)(qtile + unit * 512), 16, off, 0, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int qs = 0; qs < QSUB; ++qs) {
-      const int row = qrow0 + 16 * qs + li;
-#pragma unroll
-      for (int ch = 0; ch < G::D_CHUNKS; ++ch) {
-        u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-            qrs, (uint32_t)((row * D + 32 * ch + 8 * g) * 2), 0, 0);
-        w ^= qsign;
-        qf[qs][ch] = __builtin_bit_cast(f16x8, w);
+    // Q^T fragments, loaded once (sign-flipped when the scale is negative):
+    // into registers, or (Q_IN_LDS) the workgroup's Q rows into LDS by direct
+    // copies, chunks permuted like K rows; rows past S read as zeros.
+    f16x8 qf[QSUB][G::D_CHUNKS];
+    if constexpr (G::Q_IN_LDS) {
+      constexpr int UNITS = BLOCK_M * D * 2 / 1024;  // 1 KB copy units
+      static_assert(UNITS % WAVES == 0, "Q copy split");
+  #pragma unroll
+      for (int i = 0; i < UNITS / WAVES; ++i) {
+        const int unit = i * WAVES + wave;
+        const int slot = unit * 64 + lane;
+        const int row = slot / (D / 8);
+        const int pc = slot % (D / 8);
+        const uint32_t off = (uint32_t)(((q0 + row) * D + 8 * (pc ^ k_swizzle<D>(row))) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            qrs, (__attribute__((address_space(3))) void*)(qtile + unit * 512), 16, off, 0, 0, 0);
+      }
+    } else {
+  #pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs) {
+        const int row = qrow0 + 16 * qs + li;
+  #pragma unroll
+        for (int ch = 0; ch < G::D_CHUNKS; ++ch) {
+          u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+              qrs, (uint32_t)((row * D + 32 * ch + 8 * g) * 2), 0, 0);
+          w ^= qsign;
+          qf[qs][ch] = __builtin_bit_cast(f16x8, w);
+        }
       }
     }
-  }
-  const _Float16* qwave = qtile + 32 * qgrp * D;  // this wave's rows in the LDS Q tile
+    const _Float16* qwave = qtile + 32 * qgrp * D;  // this wave's rows in the LDS Q tile
 
-  Carrier<D> cr[QSUB];
-#pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs) {
-    cr[qs].m = NEG_BIG;
-    cr[qs].d = 0.f;
-#pragma unroll
-    for (int db = 0; db < G::D_BLOCKS; ++db) cr[qs].o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // sc: a tile's scores between Q.K^T and softmax; pf: its fp16
-  // probabilities between softmax and P.V (at D = 128 carried across the
-  // barrier into the next interval).
-  f16x8 pf[QSUB][G::KC];
-  f32x4 sc[QSUB][G::KB];
+    Carrier<D> cr[QSUB];
+  #pragma unroll
+    for (int qs = 0; qs < QSUB; ++qs) {
+      cr[qs].m = NEG_BIG;
+      cr[qs].d = 0.f;
+  #pragma unroll
+      for (int db = 0; db < G::D_BLOCKS; ++db) cr[qs].o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // sc: a tile's scores between Q.K^T and softmax; pf: its fp16
+    // probabilities between softmax and P.V (at D = 128 carried across the
+    // barrier into the next interval).
+    f16x8 pf[QSUB][G::KC];
+    f32x4 sc[QSUB][G::KB];
 
-  const int kend = CAUSAL ? min(S, q0 + BLOCK_M) : S;
-  const int n_kt = (kend + G::BN - 1) / G::BN;
-  const int n_pairs_all = (n_kt + 1) / 2;
-  // This workgroup folds tile pairs [pb, pb + n_pairs): all of them, or its
-  // split's run.
-  const int pb = SPLIT ? (int)((int64_t)split * n_pairs_all / n_splits) : 0;
-  const int n_pairs = SPLIT ? (int)((int64_t)(split + 1) * n_pairs_all / n_splits) - pb : n_pairs_all;
-  // Pairs whose tile of this wave's parity holds keys for its rows: a prefix,
-  // since tiles past S or past the wave's last query (causal) are skipped.
-  const int row_end = CAUSAL ? min(kend, qrow0 + 32) : kend;  // keys < row_end are needed
-  const int live_tiles = (row_end + G::BN - 1) / G::BN;
-  const int n_live = min(max((live_tiles - parity + 1) / 2 - pb, 0), n_pairs);
-  constexpr bool PINGPONG = G::PINGPONG;
-  // Only the last live pair of a wave can need element masks: the sequence
-  // tail is in the last tile, and a tile crossing the causal diagonal of the
-  // wave's 32 rows is the last one at or below them. (The last live pair of
-  // a split run is checked at run time.)
+    const int kend = CAUSAL ? min(S, q0 + BLOCK_M) : S;
+    const int n_kt = (kend + G::BN - 1) / G::BN;
+    const int n_pairs_all = (n_kt + 1) / 2;
+    // This workgroup folds tile pairs [pb, pb + n_pairs): all of them, or its
+    // split's run.
+    const int pb = SPLIT ? (int)((int64_t)split * n_pairs_all / n_splits) : 0;
+    const int n_pairs = SPLIT ? (int)((int64_t)(split + 1) * n_pairs_all / n_splits) - pb : n_pairs_all;
+    // Pairs whose tile of this wave's parity holds keys for its rows: a prefix,
+    // since tiles past S or past the wave's last query (causal) are skipped.
+    const int row_end = CAUSAL ? min(kend, qrow0 + 32) : kend;  // keys < row_end are needed
+    const int live_tiles = (row_end + G::BN - 1) / G::BN;
+    const int n_live = min(max((live_tiles - parity + 1) / 2 - pb, 0), n_pairs);
+    constexpr bool PINGPONG = G::PINGPONG;
+    // Only the last live pair of a wave can need element masks: the sequence
+    // tail is in the last tile, and a tile crossing the causal diagonal of the
+    // wave's 32 rows is the last one at or below them. (The last live pair of
+    // a split run is checked at run time.)
 
-  CopyPlan<D> cp;
-  make_copy_plan<D>(cp, wave, lane);
-  if (n_pairs > 0) copy_pair<D>(cp.k_off, kh, 2 * pb * G::BN, S, kring, wave);  // K of pair pb
-  if constexpr (G::PV_SAME) {
-    if (n_pairs > 0) copy_pair<D>(cp.v_off, vh, 2 * pb * G::BN, S, vring, wave);  // V of pair pb
-  }
-  wait_copies();
-  __syncthreads();
-
-  // Two-phase order (D = 128), barrier interval j (pairs counted from pb):
-  // P.V of pair j-1 and Q.K^T of pair j (MFMA), then the copies of K of pair
-  // j+1 and V of pair j, then the softmax of pair j (VALU); the
-  // probabilities stay in registers for interval j+1. The copies sit between
-  // the MFMA phase (whose LDS reads they would slow) and the softmax (which
-  // does not touch LDS). K of pair j is read from ring slot j % 2 and V of
-  // pair j-1 from slot (j-1) % 2, both copied in interval j-1. Every wave
-  // runs all n_pairs + 1 intervals; the bodies are specialised (compile-time
-  // flags) so that the steady state has no branches.
-  auto copies = [&](int j) __attribute__((always_inline)) {
-    if (j + 1 < n_pairs)
-      copy_pair<D>(cp.k_off, kh, 2 * (pb + j + 1) * G::BN, S,
-                   kring + ((j + 1) & 1) * G::SLOT_HALVES, wave);
-    if (j < n_pairs)
-      copy_pair<D>(cp.v_off, vh, 2 * (pb + j) * G::BN, S, vring + (j & 1) * G::SLOT_HALVES, wave);
-  };
-  // softmax of pair p of this wave's parity (masks possible when EDGE)
-  auto softmax_pair = [&](int p, auto edge_flag) __attribute__((always_inline)) {
-    if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(2);
-    const int key0 = (2 * (pb + p) + parity) * G::BN;
-    if constexpr (decltype(edge_flag)::value)
-      softmax_any<D, CAUSAL>(cr, sc, pf, c, key0, qrow0, S, li, g);
-    else
-      softmax_tile<D, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
-    if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(0);
-  };
-  auto mfma = [&](int j, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
-    constexpr bool PV = decltype(pv_flag)::value;
-    constexpr bool QK = decltype(qk_flag)::value;
-    const _Float16* kslot = kring + (j & 1) * G::SLOT_HALVES + parity * G::K_HALVES;
-    const _Float16* vslot = vring + ((j + 1) & 1) * G::SLOT_HALVES + parity * G::V_HALVES;
-    if constexpr (PV || QK) mfma_phase<D, PV, QK>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
-  };
-  auto end_interval = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
+    CopyPlan<D> cp;
+    make_copy_plan<D>(cp, wave, lane);
+    if (n_pairs > 0) copy_pair<D>(cp.k_off, kh, 2 * pb * G::BN, S, kring, wave);  // K of pair pb
+    if constexpr (G::PV_SAME) {
+      if (n_pairs > 0) copy_pair<D>(cp.v_off, vh, 2 * pb * G::BN, S, vring, wave);  // V of pair pb
+    }
     wait_copies();
     __syncthreads();
-  };
-  // Even waves: MFMA phase, copies, softmax of the pair just scored.
-  auto even_interval = [&](int j, auto pv_flag, auto qk_flag, auto edge_flag) __attribute__((always_inline)) {
-    mfma(j, pv_flag, qk_flag);
-    __builtin_amdgcn_sched_barrier(0);
-    copies(j);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (decltype(qk_flag)::value) softmax_pair(j, edge_flag);
-    end_interval();
-  };
-  // Odd waves run the same work half an interval out of phase: the softmax of
-  // the pair scored in the previous interval, copies, then the MFMA phase. On
-  // each SIMD one wave's softmax thus overlaps the other's MFMA phase.
-  auto odd_interval = [&](int j, auto sm_flag, auto edge_flag, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
-    if constexpr (decltype(sm_flag)::value) softmax_pair(j - 1, edge_flag);
-    __builtin_amdgcn_sched_barrier(0);
-    copies(j);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma(j, pv_flag, qk_flag);
-    end_interval();
-  };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  int j = 0;
-  if constexpr (G::PV_SAME) {
-    // Three-phase order (D = 64), interval j: Q.K^T of pair j, copies of K
-    // and V of pair j+1 (into the slots of pair j-1, read in interval j-1),
-    // softmax of pair j, P.V of pair j. Every wave runs n_pairs intervals.
-    auto copies_next = [&](int jj) __attribute__((always_inline)) {
-      if (jj + 1 < n_pairs) {
-        copy_pair<D>(cp.k_off, kh, 2 * (pb + jj + 1) * G::BN, S,
-                     kring + ((jj + 1) & 1) * G::SLOT_HALVES, wave);
-        copy_pair<D>(cp.v_off, vh, 2 * (pb + jj + 1) * G::BN, S,
-                     vring + ((jj + 1) & 1) * G::SLOT_HALVES, wave);
-      }
+
+    // Two-phase order (D = 128), barrier interval j (pairs counted from pb):
+    // P.V of pair j-1 and Q.K^T of pair j (MFMA), then the copies of K of pair
+    // j+1 and V of pair j, then the softmax of pair j (VALU); the
+    // probabilities stay in registers for interval j+1. The copies sit between
+    // the MFMA phase (whose LDS reads they would slow) and the softmax (which
+    // does not touch LDS). K of pair j is read from ring slot j % 2 and V of
+    // pair j-1 from slot (j-1) % 2, both copied in interval j-1. Every wave
+    // runs all n_pairs + 1 intervals; the bodies are specialised (compile-time
+    // flags) so that the steady state has no branches.
+    auto copies = [&](int j) __attribute__((always_inline)) {
+      if (j + 1 < n_pairs)
+        copy_pair<D>(cp.k_off, kh, 2 * (pb + j + 1) * G::BN, S,
+                     kring + ((j + 1) & 1) * G::SLOT_HALVES, wave);
+      if (j < n_pairs)
+        copy_pair<D>(cp.v_off, vh, 2 * (pb + j) * G::BN, S, vring + (j & 1) * G::SLOT_HALVES, wave);
     };
-    auto full = [&](int jj, auto edge_flag) __attribute__((always_inline)) {
-      const _Float16* kslot = kring + (jj & 1) * G::SLOT_HALVES + parity * G::K_HALVES;
-      const _Float16* vslot = vring + (jj & 1) * G::SLOT_HALVES + parity * G::V_HALVES;
-      mfma_phase<D, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+    // softmax of pair p of this wave's parity (masks possible when EDGE)
+    auto softmax_pair = [&](int p, auto edge_flag) __attribute__((always_inline)) {
+      if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(2);
+      const int key0 = (2 * (pb + p) + parity) * G::BN;
+      if constexpr (decltype(edge_flag)::value)
+        softmax_any<D, CAUSAL>(cr, sc, pf, c, key0, qrow0, S, li, g);
+      else
+        softmax_tile<D, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
+      if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(0);
+    };
+    auto mfma = [&](int j, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
+      constexpr bool PV = decltype(pv_flag)::value;
+      constexpr bool QK = decltype(qk_flag)::value;
+      const _Float16* kslot = kring + (j & 1) * G::SLOT_HALVES + parity * G::K_HALVES;
+      const _Float16* vslot = vring + ((j + 1) & 1) * G::SLOT_HALVES + parity * G::V_HALVES;
+      if constexpr (PV || QK) mfma_phase<D, PV, QK>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+    };
+    auto end_interval = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
-      copies_next(jj);
+      wait_copies();
+      __syncthreads();
+    };
+    // Even waves: MFMA phase, copies, softmax of the pair just scored.
+    auto even_interval = [&](int j, auto pv_flag, auto qk_flag, auto edge_flag) __attribute__((always_inline)) {
+      mfma(j, pv_flag, qk_flag);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_pair(jj, edge_flag);
+      copies(j);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_phase<D, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+      if constexpr (decltype(qk_flag)::value) softmax_pair(j, edge_flag);
       end_interval();
     };
-    for (; j + 1 < n_live; ++j) full(j, F_{});
-    if (j + 1 == n_live) full(j++, T_{});
-    for (; j < n_pairs; ++j) {
-      copies_next(j);
+    // Odd waves run the same work half an interval out of phase: the softmax of
+    // the pair scored in the previous interval, copies, then the MFMA phase. On
+    // each SIMD one wave's softmax thus overlaps the other's MFMA phase.
+    auto odd_interval = [&](int j, auto sm_flag, auto edge_flag, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
+      if constexpr (decltype(sm_flag)::value) softmax_pair(j - 1, edge_flag);
+      __builtin_amdgcn_sched_barrier(0);
+      copies(j);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(j, pv_flag, qk_flag);
       end_interval();
-    }
-  } else if (parity == 0 || !PINGPONG) {
-    if (n_live >= 1)
-      even_interval(j++, F_{}, T_{}, T_{});
-    else
-      even_interval(j++, F_{}, F_{}, F_{});
-    for (; j + 1 < n_live; ++j) even_interval(j, T_{}, T_{}, F_{});  // steady state
-    if (j + 1 == n_live) even_interval(j++, T_{}, T_{}, T_{});       // last live pair
-    if (j == n_live && j >= 1) even_interval(j++, T_{}, F_{}, F_{}); // its P.V
-    for (; j <= n_pairs; ++j) even_interval(j, F_{}, F_{}, F_{});    // idle: copies, barriers
-  } else {
-    // flags: softmax of the previous pair, its masks, P.V, Q.K^T
-    if (n_live >= 1)
-      odd_interval(j++, F_{}, F_{}, F_{}, T_{});
-    else
-      odd_interval(j++, F_{}, F_{}, F_{}, F_{});
-    for (; j < n_live; ++j) odd_interval(j, T_{}, F_{}, T_{}, T_{});   // steady state
-    if (j == n_live && j >= 1) odd_interval(j++, T_{}, T_{}, T_{}, F_{}); // last live pair
-    for (; j <= n_pairs; ++j) odd_interval(j, F_{}, F_{}, F_{}, F_{});  // idle
-  }
-
-  // Odd-tile waves hand their carriers to their even-tile partners.
-  float* xfer = reinterpret_cast<float*>(smem) + qgrp * 64 * G::CARRIER_FLOATS + lane;
-  if (parity == 1) {
-#pragma unroll
-    for (int qs = 0; qs < QSUB; ++qs) {
-      float* x = xfer + qs * (2 + 4 * G::D_BLOCKS) * 64;
-      x[0] = cr[qs].m;
-      x[64] = cr[qs].d;
-#pragma unroll
-      for (int db = 0; db < G::D_BLOCKS; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[(2 + 4 * db + r) * 64] = cr[qs].o[db][r];
-    }
-  }
-  __syncthreads();
-  if (parity == 1) return;
-
-  float* lse_h = lse + (int64_t)bh * S;
-  _Float16* oh = o + head;
-  const int64_t part_row0 = ((int64_t)split * BH + bh) * S;  // SPLIT: workspace rows
-#pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs) {
-    const float* x = xfer + qs * (2 + 4 * G::D_BLOCKS) * 64;
-    const float m2 = x[0];
-    const float m = __builtin_fmaxf(cr[qs].m, m2);
-    const float w1 = __builtin_amdgcn_exp2f(cr[qs].m - m);
-    const float w2 = __builtin_amdgcn_exp2f(m2 - m);
-    const float dsum = group_sum(cr[qs].d * w1 + x[64] * w2);
-    const int row = qrow0 + 16 * qs + li;
-    if constexpr (SPLIT) {
-      // A run can hold no visible key for a row (empty run, or causal keys
-      // above the row): its partial is o = 0 with weight 2^NEG_BIG = 0.
-      if (row < S) {
-        const bool empty = !(dsum > 0.0f);
-        const float inv = empty ? 0.0f : 1.0f / dsum;
-        float* po = part_o + (part_row0 + row) * D;
-#pragma unroll
-        for (int db = 0; db < G::D_BLOCKS; ++db) {
-          f32x4 val;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) val[r] = (cr[qs].o[db][r] * w1 + x[(2 + 4 * db + r) * 64] * w2) * inv;
-          *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g) = val;
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    int j = 0;
+    if constexpr (G::PV_SAME) {
+      // Three-phase order (D = 64), interval j: Q.K^T of pair j, copies of K
+      // and V of pair j+1 (into the slots of pair j-1, read in interval j-1),
+      // softmax of pair j, P.V of pair j. Every wave runs n_pairs intervals.
+      auto copies_next = [&](int jj) __attribute__((always_inline)) {
+        if (jj + 1 < n_pairs) {
+          copy_pair<D>(cp.k_off, kh, 2 * (pb + jj + 1) * G::BN, S,
+                       kring + ((jj + 1) & 1) * G::SLOT_HALVES, wave);
+          copy_pair<D>(cp.v_off, vh, 2 * (pb + jj + 1) * G::BN, S,
+                       vring + ((jj + 1) & 1) * G::SLOT_HALVES, wave);
         }
-        if (g == 0) part_lse[part_row0 + row] = empty ? NEG_BIG : m + log2f(dsum);
+      };
+      auto full = [&](int jj, auto edge_flag) __attribute__((always_inline)) {
+        const _Float16* kslot = kring + (jj & 1) * G::SLOT_HALVES + parity * G::K_HALVES;
+        const _Float16* vslot = vring + (jj & 1) * G::SLOT_HALVES + parity * G::V_HALVES;
+        mfma_phase<D, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+        __builtin_amdgcn_sched_barrier(0);
+        copies_next(jj);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax_pair(jj, edge_flag);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_phase<D, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+        end_interval();
+      };
+      for (; j + 1 < n_live; ++j) full(j, F_{});
+      if (j + 1 == n_live) full(j++, T_{});
+      for (; j < n_pairs; ++j) {
+        copies_next(j);
+        end_interval();
       }
-      continue;
+    } else if (parity == 0 || !PINGPONG) {
+      if (n_live >= 1)
+        even_interval(j++, F_{}, T_{}, T_{});
+      else
+        even_interval(j++, F_{}, F_{}, F_{});
+      for (; j + 1 < n_live; ++j) even_interval(j, T_{}, T_{}, F_{});  // steady state
+      if (j + 1 == n_live) even_interval(j++, T_{}, T_{}, T_{});       // last live pair
+      if (j == n_live && j >= 1) even_interval(j++, T_{}, F_{}, F_{}); // its P.V
+      for (; j <= n_pairs; ++j) even_interval(j, F_{}, F_{}, F_{});    // idle: copies, barriers
+    } else {
+      // flags: softmax of the previous pair, its masks, P.V, Q.K^T
+      if (n_live >= 1)
+        odd_interval(j++, F_{}, F_{}, F_{}, T_{});
+      else
+        odd_interval(j++, F_{}, F_{}, F_{}, F_{});
+      for (; j < n_live; ++j) odd_interval(j, T_{}, F_{}, T_{}, T_{});   // steady state
+      if (j == n_live && j >= 1) odd_interval(j++, T_{}, T_{}, T_{}, F_{}); // last live pair
+      for (; j <= n_pairs; ++j) odd_interval(j, F_{}, F_{}, F_{}, F_{});  // idle
     }
-    const float inv = 1.0f / dsum;
-    if (row < S) {
-#pragma unroll
-      for (int db = 0; db < G::D_BLOCKS; ++db) {
-        f16x4 h;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          h[r] = (_Float16)((cr[qs].o[db][r] * w1 + x[(2 + 4 * db + r) * 64] * w2) * inv);
-        *reinterpret_cast<f16x4*>(oh + (int64_t)row * D + 16 * db + 4 * g) = h;
+
+    // Odd-tile waves hand their carriers to their even-tile partners.
+    float* xfer = reinterpret_cast<float*>(smem) + qgrp * 64 * G::CARRIER_FLOATS + lane;
+    if (parity == 1) {
+  #pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs) {
+        float* x = xfer + qs * (2 + 4 * G::D_BLOCKS) * 64;
+        x[0] = cr[qs].m;
+        x[64] = cr[qs].d;
+  #pragma unroll
+        for (int db = 0; db < G::D_BLOCKS; ++db)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) x[(2 + 4 * db + r) * 64] = cr[qs].o[db][r];
       }
-      if (g == 0) lse_h[row] = (m + log2f(dsum)) * 0.69314718055994530942f;
+    }
+    __syncthreads();
+    if (parity == 1) return;
+
+    float* lse_h = lse + (int64_t)bh * S;
+    _Float16* oh = o + head;
+    const int64_t part_row0 = ((int64_t)split * BH + bh) * S;  // SPLIT: workspace rows
+  #pragma unroll
+    for (int qs = 0; qs < QSUB; ++qs) {
+      const float* x = xfer + qs * (2 + 4 * G::D_BLOCKS) * 64;
+      const float m2 = x[0];
+      const float m = __builtin_fmaxf(cr[qs].m, m2);
+      const float w1 = __builtin_amdgcn_exp2f(cr[qs].m - m);
+      const float w2 = __builtin_amdgcn_exp2f(m2 - m);
+      const float dsum = group_sum(cr[qs].d * w1 + x[64] * w2);
+      const int row = qrow0 + 16 * qs + li;
+      if constexpr (SPLIT) {
+        // A run can hold no visible key for a row (empty run, or causal keys
+        // above the row): its partial is o = 0 with weight 2^NEG_BIG = 0.
+        if (row < S) {
+          const bool empty = !(dsum > 0.0f);
+          const float inv = empty ? 0.0f : 1.0f / dsum;
+          float* po = part_o + (part_row0 + row) * D;
+  #pragma unroll
+          for (int db = 0; db < G::D_BLOCKS; ++db) {
+            f32x4 val;
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) val[r] = (cr[qs].o[db][r] * w1 + x[(2 + 4 * db + r) * 64] * w2) * inv;
+            *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g) = val;
+          }
+          if (g == 0) part_lse[part_row0 + row] = empty ? NEG_BIG : m + log2f(dsum);
+        }
+        continue;
+      }
+      const float inv = 1.0f / dsum;
+      if (row < S) {
+  #pragma unroll
+        for (int db = 0; db < G::D_BLOCKS; ++db) {
+          f16x4 h;
+  #pragma unroll
+          for (int r = 0; r < 4; ++r)
+            h[r] = (_Float16)((cr[qs].o[db][r] * w1 + x[(2 + 4 * db + r) * 64] * w2) * inv);
+          *reinterpret_cast<f16x4*>(oh + (int64_t)row * D + 16 * db + 4 * g) = h;
+        }
+        if (g == 0) lse_h[row] = (m + log2f(dsum)) * 0.69314718055994530942f;
+      }
+    }
+  };
+  run_tile(work.qt_first);
+  if constexpr (CAUSAL && !SPLIT) {
+    if (work.qt_second >= 0) {
+      // The second tile's copies overwrite the LDS that the first tile's
+      // epilogue reads: all waves meet before it starts.
+      __syncthreads();
+      run_tile(work.qt_second);
     }
   }
 }
