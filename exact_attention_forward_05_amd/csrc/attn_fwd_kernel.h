@@ -409,13 +409,19 @@ __device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB],
         }
       }
     }
-  float psum[QSUB];
+  // Row sums of the rounded probabilities, by dot products with ones. With
+  // SUM_ONTO_D (D = 64) a sub-tile's sum is one chain started from the
+  // lane's denominator (dnew, whose excess over d is the tile's sum); else
+  // two chains from zero (tsum), added onto d afterwards. The tile's sum is
+  // tested against the lazy-max bound.
+  constexpr bool SUM_ONTO_D = G::PV_SAME;
+  float dnew[QSUB], tsum[QSUB];
   auto expo = [&](int qs) {
     const float m = cr[qs].m;
     f32x4 p[G::KB];
 #pragma unroll
     for (int kb = 0; kb < G::KB; ++kb) p[kb] = exp_block<MASK>(sc[qs][kb], c, m, hid[qs][kb]);
-    float acc[2] = {0.0f, 0.0f};
+    float acc[2] = {SUM_ONTO_D ? cr[qs].d : 0.0f, 0.0f};
 #pragma unroll
     for (int kc = 0; kc < G::KC; ++kc) {
       f16x8 h;
@@ -426,18 +432,26 @@ __device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB],
       }
       pf[qs][kc] = h;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        acc[(e >> 1) & 1] = __builtin_amdgcn_fdot2(
-            f16x2{h[e], h[e + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc[(e >> 1) & 1], false);
+      for (int e = 0; e < 8; e += 2) {
+        const int a = SUM_ONTO_D ? 0 : (e >> 1) & 1;
+        acc[a] = __builtin_amdgcn_fdot2(f16x2{h[e], h[e + 1]},
+                                        f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc[a], false);
+      }
     }
-    psum[qs] = acc[0] + acc[1];
+    if (SUM_ONTO_D)
+      dnew[qs] = acc[0];
+    else
+      tsum[qs] = acc[0] + acc[1];
   };
 #pragma unroll
   for (int qs = 0; qs < QSUB; ++qs) expo(qs);
   // Lazy max: refresh m only when this tile's probabilities could overflow.
   bool over = false;
 #pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs) over = over || !(psum[qs] <= P_LIMIT);
+  for (int qs = 0; qs < QSUB; ++qs) {
+    const bool big = SUM_ONTO_D ? !(dnew[qs] <= cr[qs].d + P_LIMIT) : !(tsum[qs] <= P_LIMIT);
+    over = over || big;
+  }
   if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
     for (int qs = 0; qs < QSUB; ++qs) {
@@ -462,7 +476,7 @@ __device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB],
     }
   }
 #pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs) cr[qs].d += psum[qs];
+  for (int qs = 0; qs < QSUB; ++qs) cr[qs].d = SUM_ONTO_D ? dnew[qs] : cr[qs].d + tsum[qs];
 }
 
 template <int D, bool CAUSAL>
@@ -680,9 +694,13 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
                        vring + ((jj + 1) & 1) * G::SLOT_HALVES, wave);
         }
       };
-      auto full = [&](int jj, auto edge_flag) __attribute__((always_inline)) {
-        const _Float16* kslot = kring + (jj & 1) * G::SLOT_HALVES + parity * G::K_HALVES;
-        const _Float16* vslot = vring + (jj & 1) * G::SLOT_HALVES + parity * G::V_HALVES;
+      // slot_flag: the ring slot of pair jj as a compile-time constant, or
+      // -1 to take it from jj at run time.
+      auto full = [&](int jj, auto edge_flag, auto slot_flag) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slot_flag)::value;
+        const int slot = SL >= 0 ? SL : (jj & 1);
+        const _Float16* kslot = kring + slot * G::SLOT_HALVES + parity * G::K_HALVES;
+        const _Float16* vslot = vring + slot * G::SLOT_HALVES + parity * G::V_HALVES;
         mfma_phase<D, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
         __builtin_amdgcn_sched_barrier(0);
         copies_next(jj);
@@ -692,8 +710,17 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
         mfma_phase<D, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
         end_interval();
       };
-      for (; j + 1 < n_live; ++j) full(j, F_{});
-      if (j + 1 == n_live) full(j++, T_{});
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      using SR = std::integral_constant<int, -1>;
+      // Steady state unrolled by two, so that the ring slots are constant
+      // offsets of the LDS reads rather than addresses computed per interval.
+      for (; j + 2 < n_live; j += 2) {
+        full(j, F_{}, S0{});
+        full(j + 1, F_{}, S1{});
+      }
+      if (j + 1 < n_live) full(j++, F_{}, S0{});  // j is even here
+      if (j + 1 == n_live) full(j++, T_{}, SR{});
       for (; j < n_pairs; ++j) {
         copies_next(j);
         end_interval();
