@@ -6,7 +6,7 @@ device memory). Prints ONE JSON line with throughput (TFLOP/s), the kernel's
 roofline position against the dense fp16 MFMA peak, and the CPU oracle timed
 on the host as a baseline (which also checks the GPU answer).
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-ms MS] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -35,6 +35,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prewarm-ms", type=float, default=250.0,
+                    help="before the warmup steps, run the step back to back for this long "
+                         "so that the GPU clock reaches its sustained level (0: off); "
+                         "sweep and split-KV points get up to 100 ms each")
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (for profiler runs)")
@@ -177,6 +181,24 @@ def raw_step(entry, q, k, v, o, lse, w, stream, extra=()):
 LAUNCH_GROUP = 4  # launches between two events
 
 
+def prewarm(step, ms):
+    """Run ``step`` back to back for at least ``ms`` milliseconds of wall time
+    (batches of 16, one synchronisation per batch). The MI355X shader clock
+    ramps over tens of milliseconds of sustained load: without this the first
+    few hundred launches of a run are up to 20% slower than the sustained
+    rate. Returns {"ms": elapsed, "steps": launches}."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while ms > 0 and (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(16):
+            step()
+        n += 16
+        torch.cuda.synchronize()
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "steps": n}
+
+
 def time_launches(step, stream, steps):
     """Launch ``step`` ``steps`` times back to back, with a pair of HIP events
     on the launch stream around every group of LAUNCH_GROUP launches (an event
@@ -224,7 +246,7 @@ def time_cold(step, dev, stream, steps):
             "us_median": round(float(np.median(ms)) * 1e3, 3), "launches": steps}
 
 
-def run_sweep(attn, dev, stream, steps):
+def run_sweep(attn, dev, stream, steps, prewarm_ms):
     """Kernel time over the sequence-length sweep (B1 H8 D64; S = 4k, 8k, 16k;
     non-causal and causal)."""
     import torch
@@ -240,6 +262,7 @@ def run_sweep(attn, dev, stream, steps):
 
         attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
         step = raw_step("attn_fwd", q, k, v, o, lse, w, stream)
+        prewarm(step, prewarm_ms)
         for _ in range(5):
             step()
         durs, _ = time_launches(step, stream, steps)
@@ -255,7 +278,7 @@ def run_sweep(attn, dev, stream, steps):
     return out
 
 
-def run_splitkv(attn, dev, stream, steps):
+def run_splitkv(attn, dev, stream, steps, prewarm_ms):
     """Single-pass vs split-KV (split count from the library's heuristic) on
     workloads that leave CUs idle or unbalanced in one pass."""
     import torch
@@ -282,6 +305,7 @@ def run_splitkv(attn, dev, stream, steps):
 
         rec = {"workload": name, "n_splits": ns}
         for tag, fn in (("single_pass", single), ("splitkv", split)):
+            prewarm(fn, prewarm_ms)
             for _ in range(5):
                 fn()
             durs, _ = time_launches(fn, stream, steps)
@@ -339,6 +363,8 @@ def main():
         log(f"copy calibration: 3 copies of {nbytes} bytes")
         del src, dst
 
+    pre = prewarm(step, args.prewarm_ms)
+    log(f"prewarm: {pre['steps']} launches in {pre['ms']} ms")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
@@ -361,6 +387,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm": pre,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -394,8 +421,9 @@ def main():
         result["cold"] = time_cold(step, dev, stream, min(args.steps, 50))
         log(f"cold launches: {result['cold']}")
     if not args.no_sweep:
-        result["sweep"] = run_sweep(attn, dev, stream, args.sweep_steps)
-        result["splitkv"] = run_splitkv(attn, dev, stream, args.sweep_steps)
+        point_ms = min(args.prewarm_ms, 100.0)
+        result["sweep"] = run_sweep(attn, dev, stream, args.sweep_steps, point_ms)
+        result["splitkv"] = run_splitkv(attn, dev, stream, args.sweep_steps, point_ms)
     if not args.no_cpu_baseline:
         log("CPU oracle leg ...")
         o_np = o.cpu().numpy()
