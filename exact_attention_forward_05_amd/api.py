@@ -75,36 +75,59 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float
 
 BLOCK_M = 128     # query rows per workgroup
 PAIR_KEYS = 128   # keys per tile pair (two 64-key tiles)
-# Rough per-interval time (one tile pair per wave) and HBM rate used to price
-# the combine; only the choice between split counts depends on them.
-_INTERVAL_US = {64: 1.4, 128: 2.4}
+# Per-interval time (one tile pair per wave), fixed work per query tile (Q
+# load, first copies, epilogue; in intervals), and the combine's HBM rate and
+# fixed cost. Fitted to split-KV timings of causal B1 H8 S4096/S8192 D64,
+# B1 H2 S8192 D128, B1 H4 S4096 D128 and B2 H4 S2048 D64 at 1-6 runs on
+# MI355X (sustained clock); only the choice between split counts depends on
+# them (the chosen count was within 1.5% of the fastest on those shapes).
+_INTERVAL_US = {64: 1.05, 128: 1.6}
+_TILE_FIXED = 1.0
 _COMBINE_GBS = 4000.0
-_COMBINE_FIXED_US = 4.0
+_COMBINE_FIXED_US = 3.0
 _SPLIT_CHOICES = (1, 2, 3, 4, 6, 8, 12, 16)
 
 
 @functools.lru_cache(maxsize=256)
+def _workgroup_costs(B: int, H: int, S: int, causal: bool, s: int, n_cus: int) -> list:
+    """Cost of every workgroup of a launch with ``s`` runs (one pass when
+    s == 1), in key-tile-pair intervals plus a fixed cost per query tile that
+    a workgroup loads, following the kernel's work orders: each query tile's
+    pairs are cut into ``s`` runs; a causal single pass folds mirror pairs of
+    tiles (n_qtiles + 1 pairs, two tiles loaded) when that still fills the
+    CUs."""
+    n_qt = -(-S // BLOCK_M)
+    pairs = [i + 1 if causal else n_qt for i in range(n_qt)]
+    costs = []
+    if s == 1 and causal and B * H * ((n_qt + 1) // 2) >= n_cus:
+        for u in range((n_qt + 1) // 2):
+            a = n_qt - 1 - u
+            costs.append(pairs[a] + _TILE_FIXED if u == a
+                         else pairs[a] + pairs[u] + 2 * _TILE_FIXED)
+    else:
+        for p in pairs:
+            for r in range(s):
+                costs.append((r + 1) * p // s - r * p // s + _TILE_FIXED)
+    return costs * (B * H)
+
+
 def choose_splits(B: int, H: int, S: int, D: int, causal: bool, n_cus: int = 256) -> int:
     """Split count for attn_fwd_splitkv from a small cost model.
 
     Each workgroup (one per CU: its LDS use allows no second) costs its run of
-    tile pairs plus two intervals of fixed work; workgroups are placed longest
-    first on the least loaded CU; a split count above one adds the partial
+    tile pairs plus a fixed cost per query tile it loads
+    (:func:`_workgroup_costs`); workgroups are placed in launch order, largest
+    first, on the least loaded CU; a split count above one adds the partial
     results' HBM traffic and a second launch. Returns the cheapest count.
     """
     n_qt = -(-S // BLOCK_M)
-    pairs = [-(-min(S, BLOCK_M * (i + 1) if causal else S) // PAIR_KEYS) for i in range(n_qt)]
     if B * H * n_qt >= 4 * n_cus and not causal:
         return 1
     best, best_us = 1, math.inf
     for s in _SPLIT_CHOICES:
-        if s > max(pairs):
+        if s > max(1, n_qt):  # never more runs than the longest tile has pairs
             break
-        costs = []
-        for p in pairs:
-            runs = [(r + 1) * p // s - r * p // s for r in range(s)]
-            costs += [run + 2 for run in runs]
-        costs = sorted(costs * (B * H), reverse=True)
+        costs = sorted(_workgroup_costs(B, H, S, causal, s, n_cus), reverse=True)
         if len(costs) > 200000:
             break
         loads = [0.0] * min(n_cus, len(costs))
