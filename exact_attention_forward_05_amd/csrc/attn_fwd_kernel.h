@@ -12,11 +12,12 @@
 // one (batch, head). Waves 0-3 take 32 rows each and fold the even 64-key
 // tiles; waves 4-7 take the same rows and fold the odd tiles. The two waves on
 // one SIMD therefore work on independent data and can fill each other's
-// stalls (a single wave serialises its own MFMA and VALU instructions on
-// gfx950, and a softmax barely progresses while the other wave streams
-// MFMAs, so the interval order is chosen per head dimension; see the schedule
-// note at the kernel). At the end each odd-tile wave hands its carrier to its
-// partner through LDS and the two are merged.
+// stalls. (gfx950 runs independent FMAs, exponentials and conversions beside
+// an MFMA stream, but the v_dot2 row sums wait for it, and the MFMA stream is
+// itself limited by its LDS operand reads; the interval order is chosen per
+// head dimension by measurement, see the schedule note at the kernel.) At the
+// end each odd-tile wave hands its carrier to its partner through LDS and the
+// two are merged.
 //
 // MFMA: v_mfma_f32_16x16x32_f16. Lane l = 16*g + i (g = 0..3, i = 0..15):
 //   A: row i, contraction slots (g, 0..7); B: column i, slots (g, 0..7);
@@ -94,10 +95,10 @@ struct Geometry {
   // output accumulators: the workgroup's Q rows are staged in LDS instead.
   static constexpr bool Q_IN_LDS = D == 128;
   // Odd waves run half an interval out of phase with even waves (softmax
-  // against the other wave's MFMA phase). Each 16x16x32 MFMA blocks the other
-  // wave's VALU issue for about half its 16 cycles, so this pays only where
-  // the MFMA phase is long next to the softmax: at D = 128 (5% on causal
-  // B2 H16 S8192), not at D = 64 (5% slower).
+  // against the other wave's MFMA phase). This pays only where the MFMA phase
+  // is long next to the softmax: at D = 128 (5% on causal B2 H16 S8192), not
+  // at D = 64 (5% slower, and no faster with fp32-add row sums in place of
+  // the v_dot2 sums that wait for the other wave's MFMAs).
   static constexpr bool PINGPONG = D == 128;
   // At D = 64 a tile's P.V runs in the same interval as its Q.K^T and
   // softmax (three phases, V copied one interval earlier): the SIMD's two
