@@ -38,8 +38,9 @@
 // The running max is updated lazily: a tile is first exponentiated against the
 // current m; only if some lane's probabilities could overflow (their fp16 sum
 // exceeds P_LIMIT, or is not finite) does the wave compute the tile max,
-// rescale o and d, and redo the tile. Because o and d always share one m, the
-// result is the same softmax; probabilities up to P_LIMIT keep fp16's
+// rescale o and d, and redo the tile, for the 16-row sub-tiles concerned.
+// Because o and d always share one m, the result is the same softmax; m never
+// exceeds the true row max, and probabilities up to P_LIMIT keep fp16's
 // relative precision. The row sum adds the fp16-rounded probabilities
 // (v_dot2), so d normalises exactly the weights the P.V product used.
 //
@@ -72,7 +73,9 @@ constexpr int WAVES = 2 * QGROUPS;    // even-tile and odd-tile waves
 constexpr int THREADS = WAVES * 64;
 constexpr int QSUB = 2;               // 16-row query sub-tiles per wave
 constexpr float NEG_BIG = -1.0e30f;   // finite stand-in for -infinity
-constexpr float P_LIMIT = 16384.0f;   // lazy-max bound on a lane's fp16 tile sum
+// Lazy-max bound on a lane's tile sum: every probability stays below it, and
+// so below fp16's largest finite value (65504) with room for rounding.
+constexpr float P_LIMIT = 32768.0f;
 constexpr uint32_t BUF_FLAGS = 0x00020000u;  // raw buffer, 32-bit data format
 
 template <int D>
@@ -446,16 +449,20 @@ __device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB],
   };
 #pragma unroll
   for (int qs = 0; qs < QSUB; ++qs) expo(qs);
-  // Lazy max: refresh m only when this tile's probabilities could overflow.
+  // Lazy max: refresh m only when this tile's probabilities could overflow,
+  // and only for the sub-tiles whose lanes exceed the bound (one test on the
+  // common path; with peaked scores one row in 256 often trips it, and every
+  // wave of the workgroup then waits for that redo at the barrier).
+  auto big = [&](int qs) {
+    return SUM_ONTO_D ? !(dnew[qs] <= cr[qs].d + P_LIMIT) : !(tsum[qs] <= P_LIMIT);
+  };
   bool over = false;
 #pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs) {
-    const bool big = SUM_ONTO_D ? !(dnew[qs] <= cr[qs].d + P_LIMIT) : !(tsum[qs] <= P_LIMIT);
-    over = over || big;
-  }
+  for (int qs = 0; qs < QSUB; ++qs) over = over || big(qs);
   if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
     for (int qs = 0; qs < QSUB; ++qs) {
+      if (__builtin_amdgcn_ballot_w64(big(qs)) == 0) continue;
       float tmax = NEG_BIG;
 #pragma unroll
       for (int kb = 0; kb < G::KB; ++kb) {

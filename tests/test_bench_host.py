@@ -34,7 +34,9 @@ def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     text = k.read_text()
     k.write_text("// an added comment\n/* and a block\n comment */\n" + text.replace("\n", "\n\n", 3))
     assert bench.kernel_source_hash() == h0
-    k.write_text(text.replace("P_LIMIT = 16384.0f", "P_LIMIT = 8192.0f", 1))
+    changed = text.replace("BLOCK_M = 128;", "BLOCK_M = 64;", 1)
+    assert changed != text  # the edit below is a code change
+    k.write_text(changed)
     assert bench.kernel_source_hash() != h0
 
 
