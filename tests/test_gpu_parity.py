@@ -97,6 +97,30 @@ def test_large_workload_sampled_rows(name):
 
 # ---------------------------------------------------------------- closed forms
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_refresh_in_one_sub_tile(D, causal):
+    """Rows whose scores jump late in the sequence next to rows whose scores
+    stay flat: every 32-row block has a peaked first half (Q x 4) and a flat
+    second half (Q / 2), and three keys mid-sequence are scaled by 4. The
+    peaked rows must refresh their running max at those keys while the flat
+    rows of the same waves keep theirs; both must match the oracle."""
+    B, H, S = 1, 2, 700
+    _announce(f"lazy max one sub-tile D{D} causal={causal}")
+    q, k, v = make_qkv(B, H, S, D, 9100 + D + int(causal))
+    rows = np.arange(S)
+    q = q.astype(np.float32)
+    q[:, :, (rows % 32) < 16, :] *= 4.0      # exact in fp16 (powers of two)
+    q[:, :, (rows % 32) >= 16, :] *= 0.5
+    k = k.astype(np.float32)
+    k[:, :, [200, 450, 601], :] *= 4.0
+    q, k = q.astype(np.float16), k.astype(np.float16)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    o, l = run_gpu(q, k, v, scale, causal)
+    O, L = oracle.sdpa_forward(q, k, v, scale, causal)
+    compare(o, l, O, L, f"lazy max D{D} causal={causal}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_zero_scale_gives_mean_of_visible_v(causal):
     B, H, S, D = 1, 2, 200, 64
