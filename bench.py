@@ -380,6 +380,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (avg_ms * 1e-3) / 1e12
+    traffic = profiled_traffic(w.name)
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -404,7 +405,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4),
-                     "traffic": profiled_traffic(w.name),
+                     "traffic": traffic,
                      "kernel": f"attn_fwd_kernel<{w.D},{str(w.causal).lower()}>",
                      "algorithmic_flops_per_launch": w.flops,
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
@@ -413,7 +414,11 @@ def main():
                       "us_at_exp_peak": round(visible_scores(w) / EXP_PER_S * 1e6, 3),
                       "frac": round(visible_scores(w) / EXP_PER_S / (avg_ms * 1e-3), 4)},
         "hbm_bound": {"us_at_hbm_peak": round(w.algorithmic_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 3),
-                      "frac": round(w.algorithmic_bytes / (avg_ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)},
+                      "frac": round(w.algorithmic_bytes / (avg_ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+                      # GB/s of the algorithmic bytes, and of the profiled HBM traffic
+                      "algorithmic_gbs": round(w.algorithmic_bytes / (avg_ms * 1e-3) / 1e9, 1),
+                      "traffic_gbs": (None if traffic is None
+                                      else round(traffic / (avg_ms * 1e-3) / 1e9, 1))},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }
