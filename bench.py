@@ -47,8 +47,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the sequence-length sweep (4k/8k/16k, B1 H8 D64) and the "
-                         "split-KV comparison")
+                    help="skip the five-configuration timings, the sequence-length sweep "
+                         "(4k/8k/16k, B1 H8 D64) and the split-KV comparison")
     ap.add_argument("--sweep-steps", type=int, default=30,
                     help="timed launches per sweep point")
     ap.add_argument("--cold", action="store_true",
@@ -246,35 +246,57 @@ def time_cold(step, dev, stream, steps):
             "us_median": round(float(np.median(ms)) * 1e3, 3), "launches": steps}
 
 
+def time_workload(attn, dev, stream, name, steps, prewarm_ms):
+    """Kernel time of one workload: pre-warm, 5 launches, then `steps` timed
+    launches in event-bracketed groups. Returns the record for the JSON line."""
+    import torch
+
+    from testkit import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[name]
+    q, k, v = (torch.from_numpy(x).to(dev) for x in workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+
+    attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+    step = raw_step("attn_fwd", q, k, v, o, lse, w, stream)
+    prewarm(step, prewarm_ms)
+    for _ in range(5):
+        step()
+    durs, _ = time_launches(step, stream, steps)
+    mean_ms = float(durs.mean())
+    rec = {"workload": name, "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": w.causal,
+           "us_mean": round(mean_ms * 1e3, 3),
+           "us_median": round(float(np.median(durs)) * 1e3, 3),
+           "tflops": round(w.flops / (mean_ms * 1e-3) / 1e12, 2),
+           "pct_of_peak": round(100 * w.flops / (mean_ms * 1e-3) / 1e12
+                                / PEAK_FP16_MFMA_TFLOPS, 2)}
+    del q, k, v, o, lse
+    return rec
+
+
 def run_sweep(attn, dev, stream, steps, prewarm_ms):
     """Kernel time over the sequence-length sweep (B1 H8 D64; S = 4k, 8k, 16k;
     non-causal and causal)."""
-    import torch
-
-    from testkit import SWEEP, WORKLOADS, workload_inputs
+    from testkit import SWEEP
 
     out = []
     for (S, causal), name in sorted(SWEEP.items(), key=lambda kv: (kv[0][1], kv[0][0])):
-        w = WORKLOADS[name]
-        q, k, v = (torch.from_numpy(x).to(dev) for x in workload_inputs(w))
-        o = torch.empty_like(q)
-        lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
-
-        attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
-        step = raw_step("attn_fwd", q, k, v, o, lse, w, stream)
-        prewarm(step, prewarm_ms)
-        for _ in range(5):
-            step()
-        durs, _ = time_launches(step, stream, steps)
-        mean_ms = float(durs.mean())
+        rec = time_workload(attn, dev, stream, name, steps, prewarm_ms)
         out.append({"workload": name, "S": S, "causal": causal,
-                    "us_mean": round(mean_ms * 1e3, 3),
-                    "us_median": round(float(np.median(durs)) * 1e3, 3),
-                    "tflops": round(w.flops / (mean_ms * 1e-3) / 1e12, 2),
-                    "pct_of_peak": round(100 * w.flops / (mean_ms * 1e-3) / 1e12
-                                         / PEAK_FP16_MFMA_TFLOPS, 2)})
+                    **{k: rec[k] for k in ("us_mean", "us_median", "tflops", "pct_of_peak")}})
         log(f"sweep {name}: {out[-1]['us_mean']} us, {out[-1]['tflops']} TFLOP/s")
-        del q, k, v, o, lse
+    return out
+
+
+def run_configs(attn, dev, stream, steps, prewarm_ms):
+    """Kernel time of each of the five problem configurations."""
+    from testkit import CONFIGS
+
+    out = []
+    for name in CONFIGS:
+        out.append(time_workload(attn, dev, stream, name, steps, prewarm_ms))
+        log(f"config {name}: {out[-1]['us_mean']} us, {out[-1]['tflops']} TFLOP/s")
     return out
 
 
@@ -427,6 +449,7 @@ def main():
         log(f"cold launches: {result['cold']}")
     if not args.no_sweep:
         point_ms = min(args.prewarm_ms, 100.0)
+        result["configs"] = run_configs(attn, dev, stream, args.sweep_steps, point_ms)
         result["sweep"] = run_sweep(attn, dev, stream, args.sweep_steps, point_ms)
         result["splitkv"] = run_splitkv(attn, dev, stream, args.sweep_steps, point_ms)
     if not args.no_cpu_baseline:

@@ -86,6 +86,11 @@ SPLITKV_BENCH = ("single_head_b1h1s16384d64", "sweep_causal_b1h8s4096d64")
 
 HEADLINE = "sdpa_b1h8s4096d64"
 
+# The five problem configurations: the tiny listing case, the headline, the
+# long sequence, causal D = 128, and causal D = 128 with peaked scores.
+CONFIGS = ("listing_b1h4s128d64", "sdpa_b1h8s4096d64", "long_b1h8s16384d64",
+           "causal_b2h16s8192d128", "peaked_causal_b4h32s4096d128")
+
 # Sequence-length sweep at batch 1, 8 heads, head_dim 64: (S, causal) -> name.
 SWEEP = {
     (4096, False): "sdpa_b1h8s4096d64",

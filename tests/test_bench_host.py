@@ -68,3 +68,21 @@ def test_work_counts(name):
     full = 4.0 * w.B * w.H * w.S * w.S * w.D
     assert w.flops == (full / 2 if w.causal else full)
     assert w.algorithmic_bytes == 8 * w.B * w.H * w.S * w.D + 4 * w.B * w.H * w.S
+
+
+def test_configs_are_the_five_problem_shapes():
+    """The bench times these five; their shapes, masks, scales and input
+    scaling are the problem configurations."""
+    import numpy as np
+
+    from testkit import CONFIGS, WORKLOADS
+
+    want = [(1, 4, 128, 64, False, 1.0), (1, 8, 4096, 64, False, 1.0),
+            (1, 8, 16384, 64, False, 1.0), (2, 16, 8192, 128, True, 1.0),
+            (4, 32, 4096, 128, True, 3.0)]
+    got = [(WORKLOADS[n].B, WORKLOADS[n].H, WORKLOADS[n].S, WORKLOADS[n].D, WORKLOADS[n].causal,
+            WORKLOADS[n].qk_mult) for n in CONFIGS]
+    assert got == want
+    for n in CONFIGS:
+        w = WORKLOADS[n]
+        assert w.scale == float(np.float32(1.0 / np.sqrt(w.D)))
