@@ -61,7 +61,7 @@ def log(msg):
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("attn_fwd_kernel.h", "work_order.h", "attn_fwd.hip")
+KERNEL_SOURCES = ("attn_fwd_kernel.h", "work_order.h", "plan.h", "attn_fwd.hip")
 
 
 def kernel_source_hash() -> str:

@@ -114,7 +114,9 @@ def _workgroup_costs(B: int, H: int, S: int, causal: bool, s: int, n_cus: int) -
 def choose_splits(B: int, H: int, S: int, D: int, causal: bool, n_cus: int = 256) -> int:
     """Split count for attn_fwd_splitkv from a small cost model.
 
-    Each workgroup (one per CU: its LDS use allows no second) costs its run of
+    Each workgroup (one per CU: at D = 64 the registers of its eight waves,
+    two per SIMD, and at D = 128 its 160 KB of LDS leave room for no second)
+    costs its run of
     tile pairs plus a fixed cost per query tile it loads
     (:func:`_workgroup_costs`); workgroups are placed in launch order, largest
     first, on the least loaded CU; a split count above one adds the partial

@@ -17,7 +17,7 @@ LIB_NAME = "libattn_fwd.so"
 ARCH = "gfx950"
 
 SOURCES = ["attn_fwd.hip"]
-HEADERS = ["attn_fwd_kernel.h", "work_order.h"]
+HEADERS = ["attn_fwd_kernel.h", "work_order.h", "plan.h"]
 
 # -packed-fp32-ops: hipcc must not form packed fp32 VALU ops from scalar code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",

@@ -569,7 +569,9 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
         const int slot = unit * 64 + lane;
         const int row = slot / (D / 8);
         const int pc = slot % (D / 8);
-        const uint32_t off = (uint32_t)(((q0 + row) * D + 8 * (pc ^ k_swizzle<D>(row))) * 2);
+        // Rows past S (up to S + 127) fall outside the descriptor's range and
+        // read as zeros; offsets are unsigned 32-bit (S * D * 2 < 2^31).
+        const uint32_t off = ((uint32_t)(q0 + row) * D + 8u * (uint32_t)(pc ^ k_swizzle<D>(row))) * 2u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             qrs, (__attribute__((address_space(3))) void*)(qtile + unit * 512), 16, off, 0, 0, 0);
       }
@@ -580,7 +582,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   #pragma unroll
         for (int ch = 0; ch < G::D_CHUNKS; ++ch) {
           u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-              qrs, (uint32_t)((row * D + 32 * ch + 8 * g) * 2), 0, 0);
+              qrs, ((uint32_t)row * D + 32u * ch + 8u * g) * 2u, 0, 0);
           w ^= qsign;
           qf[qs][ch] = __builtin_bit_cast(f16x8, w);
         }
@@ -830,6 +832,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
 // M = max_s l_s, w_s = 2^(l_s - M), O = sum_s w_s o_s / sum_s w_s and
 // LSE = (M + log2 sum_s w_s) ln 2. One thread per row and 4 columns; reads and
 // writes are contiguous along the row (HBM-bound).
+// The grid strides over the rows, so any row count fits a bounded grid.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
@@ -837,26 +840,28 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
                                                            float* __restrict__ lse, int64_t rows,
                                                            int n_splits) {
   constexpr int TPR = D / 4;  // threads per row
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = t / TPR;
-  const int c4 = (int)(t % TPR);
-  if (row >= rows) return;
-  float M = NEG_BIG;
-  for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, part_lse[s * rows + row]);
-  float W = 0.0f;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int s = 0; s < n_splits; ++s) {
-    const float w = __builtin_amdgcn_exp2f(part_lse[s * rows + row] - M);
-    const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + (s * rows + row) * D + 4 * c4);
-    W += w;
-    acc += w * v;
-  }
-  const float inv = 1.0f / W;
-  f16x4 h;
+  const int64_t items = rows * TPR;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < items;
+       t += (int64_t)gridDim.x * 256) {
+    const int64_t row = t / TPR;
+    const int c4 = (int)(t % TPR);
+    float M = NEG_BIG;
+    for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, part_lse[s * rows + row]);
+    float W = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < n_splits; ++s) {
+      const float w = __builtin_amdgcn_exp2f(part_lse[s * rows + row] - M);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + (s * rows + row) * D + 4 * c4);
+      W += w;
+      acc += w * v;
+    }
+    const float inv = 1.0f / W;
+    f16x4 h;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) h[r] = (_Float16)(acc[r] * inv);
-  *reinterpret_cast<f16x4*>(o + row * D + 4 * c4) = h;
-  if (c4 == 0) lse[row] = (M + log2f(W)) * 0.69314718055994530942f;
+    for (int r = 0; r < 4; ++r) h[r] = (_Float16)(acc[r] * inv);
+    *reinterpret_cast<f16x4*>(o + row * D + 4 * c4) = h;
+    if (c4 == 0) lse[row] = (M + log2f(W)) * 0.69314718055994530942f;
+  }
 }
 
 }  // namespace attn

@@ -59,3 +59,38 @@ def sample_rows(S: int, rng: np.random.Generator, n_random: int = 24):
     rows = {r for r in fixed if 0 <= r < S}
     rows |= set(int(x) for x in rng.integers(0, S, size=n_random))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def oracle_full(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
+                workers: int = 16, row_chunk: int = 1024):
+    """The oracle over every head and row, its per-row evaluations spread over
+    host threads: tasks of (head, block of rows), each one call of
+    oracle.sdpa_rows with BLAS limited to one thread per task. Only the order
+    in which rows are evaluated differs from oracle.sdpa_forward."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    B, H, S, D = q.shape
+    O = np.empty((B, H, S, D), dtype=np.float64)
+    L = np.empty((B, H, S), dtype=np.float64)
+    tasks = [(b, h, lo) for b in range(B) for h in range(H) for lo in range(0, S, row_chunk)]
+
+    def run(t):
+        b, h, lo = t
+        rows = np.arange(lo, min(S, lo + row_chunk))
+        O[b, h, lo:lo + len(rows)], L[b, h, lo:lo + len(rows)] = oracle.sdpa_rows(
+            q, k, v, scale, causal, b, h, rows)
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1, "blas")
+    except Exception:  # threadpoolctl missing: BLAS keeps its own threads
+        limit = None
+    try:
+        with ThreadPoolExecutor(max(1, workers)) as ex:
+            list(ex.map(run, tasks))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    return O, L

@@ -156,3 +156,15 @@ def test_product_package_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\boracle\b", text), f"{f} mentions the oracle"
                 assert "testkit" not in text, f"{f} uses the test input generator"
+
+
+def test_grid_beyond_one_dispatch_is_rejected_before_launch():
+    # 2^20 heads of 4096 rows: 2^25 workgroups x 512 threads > 2^32 work-items.
+    # Fits the 2^40-element limit, so only the grid check can refuse it.
+    rc = _lib.attn_fwd(A, B_, C, O, L, 1 << 10, 1 << 10, 4096, 64, 0.125, 0, 0)
+    assert _lib.STATUS_NAMES[rc] == "ATTN_ERR_SHAPE"
+    assert "work-items" in _lib.load().attn_last_error().decode()
+    # the split-KV launch multiplies the grid by n_splits (workspace size is a
+    # fake figure: nothing is enqueued)
+    rc = _split(n_splits=64, ws_bytes=1 << 62, B=1, H=1 << 11, S=8192)
+    assert _lib.STATUS_NAMES[rc] == "ATTN_ERR_SHAPE"
