@@ -26,6 +26,10 @@ _SIGNATURES = [
      [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
       ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("attn_fwd_splitkv_noalloc", ctypes.c_int,
+     [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+      ctypes.c_int, ctypes.c_void_p]),
     ("attn_fwd_splitkv_workspace_size", ctypes.c_size_t,
      [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     ("attn_status_string", ctypes.c_char_p, [ctypes.c_int]),
@@ -78,6 +82,17 @@ def attn_fwd_splitkv(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: in
     return load().attn_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D,
                                    ctypes.c_float(scale), causal, n_splits, ws_ptr, ws_bytes,
                                    stream)
+
+
+def attn_fwd_splitkv_noalloc(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int,
+                             H: int, S: int, D: int, scale: float, causal: int, n_splits: int,
+                             stream: int) -> int:
+    """Raw call of the allocation-free split-KV entry point; returns the status."""
+    return load().attn_fwd_splitkv_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D,
+                                           ctypes.c_float(scale), causal, n_splits, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
 
 
 def splitkv_workspace_size(B: int, H: int, S: int, D: int, n_splits: int) -> int:

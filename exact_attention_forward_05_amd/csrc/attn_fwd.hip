@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "attn_fwd.h"
 #include "attn_fwd_kernel.h"
@@ -85,6 +86,41 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
   return attn::plan::make_launch(B, H, S, D, causal, n_splits, &L, msg());
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free split-KV entry point. Each device
+// holds its own copy of this array from the library's load until the process
+// ends. Host code must never pass `scratch` itself to a kernel (on the host
+// the name is only a stand-in for the symbol): its device address is looked up
+// once per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+constexpr int MAX_DEVICES = 64;
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+void* g_scratch_ptr[MAX_DEVICES] = {};
+std::mutex g_scratch_mutex;
+
+// Device address of this device's scratch array (looked up on the first call
+// on the device, with the device current). ATTN_OK or ATTN_ERR_HIP.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess)
+    return attn::plan::fail(msg(), ATTN_ERR_HIP, "hipGetDevice failed: %s",
+                            hipGetErrorString(err));
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return attn::plan::fail(msg(), ATTN_ERR_HIP, "device %d is outside the %d supported", dev,
+                            MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p)
+      return attn::plan::fail(msg(), ATTN_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s",
+                              hipGetErrorString(err));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,6 +156,29 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                               workspace_size, need);
   }
   return dispatch(q, k, v, o, lse, B, H, S, D, scale, causal, n_splits, workspace, stream);
+}
+
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int S, int D, float scale, int causal, int n_splits,
+                             void* stream) {
+  g_last_error[0] = '\0';
+  const int rc = check_common(q, k, v, o, lse, B, H, S, D, scale, causal, n_splits);
+  if (rc != ATTN_OK) return rc;
+  void* ws = nullptr;
+  if (n_splits > 1) {
+    const size_t need = attn::plan::workspace_size(B, H, S, D, n_splits);
+    if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+      return attn::plan::fail(msg(), ATTN_ERR_ARG,
+                              "n_splits=%d needs %zu bytes of partial results, more than the "
+                              "%u-byte static scratch buffer; use attn_fwd_splitkv with a "
+                              "workspace, or fewer splits", n_splits, need,
+                              (unsigned)ATTN_NOALLOC_SCRATCH_BYTES);
+    const int src = scratch_of_current_device(&ws);
+    if (src != ATTN_OK) return src;
+  }
+  // Every partial result the combine kernel reads is written by the split
+  // kernel of the same call first, so the scratch needs no clearing.
+  return dispatch(q, k, v, o, lse, B, H, S, D, scale, causal, n_splits, ws, stream);
 }
 
 const char* attn_status_string(int status) {

@@ -118,6 +118,36 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  * for n_splits > 1; 0 when n_splits == 1 or an argument is out of range. */
 size_t attn_fwd_splitkv_workspace_size(int B, int H, int S, int D, int n_splits);
 
+/* Size of the static device scratch buffer of attn_fwd_splitkv_noalloc. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * attn_fwd_splitkv_noalloc -- attn_fwd_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the partial results go to a static device
+ * array of ATTN_NOALLOC_SCRATCH_BYTES owned by the library instead of a
+ * caller workspace. The call allocates nothing; on the first call on a device
+ * (with that device current) it looks up the array's device address once.
+ *
+ *  q ... n_splits : as attn_fwd_splitkv (same layouts, checks and results:
+ *                   the same kernels run, so outputs equal attn_fwd_splitkv's
+ *                   with the same n_splits bit for bit).
+ *  stream         : hipStream_t as void* (NULL = default stream).
+ *
+ *  Returns ATTN_ERR_ARG when attn_fwd_splitkv_workspace_size(B, H, S, D,
+ *  n_splits) exceeds ATTN_NOALLOC_SCRATCH_BYTES (nothing is enqueued), and
+ *  ATTN_ERR_HIP if the scratch address cannot be looked up.
+ *
+ *  Every call on one device shares that device's scratch array, which keeps
+ *  the last call's contents (each call writes every partial it reads, so no
+ *  clearing is needed): calls with n_splits > 1 that overlap in time on one
+ *  device (on different streams, or from different threads) race and must be
+ *  serialised by the caller.
+ */
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int S, int D, float scale, int causal, int n_splits,
+                             void* stream);
+
 /* Static English name of a status code ("ATTN_OK", ...); never NULL. */
 const char* attn_status_string(int status);
 

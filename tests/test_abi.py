@@ -168,3 +168,24 @@ def test_grid_beyond_one_dispatch_is_rejected_before_launch():
     # fake figure: nothing is enqueued)
     rc = _split(n_splits=64, ws_bytes=1 << 62, B=1, H=1 << 11, S=8192)
     assert _lib.STATUS_NAMES[rc] == "ATTN_ERR_SHAPE"
+
+
+NOALLOC_INVALID = [
+    ("null o", dict(o=0), "ATTN_ERR_NULL"),
+    ("D=96", dict(D=96), "ATTN_ERR_UNSUPPORTED"),
+    ("n_splits=0", dict(n_splits=0), "ATTN_ERR_ARG"),
+    ("n_splits=65", dict(n_splits=65), "ATTN_ERR_ARG"),
+    # 8 splits of 8 heads x 65536 rows need 8*8*65536*65*4 bytes > 32 MiB
+    ("beyond static scratch", dict(H=8, S=1 << 16, n_splits=8), "ATTN_ERR_ARG"),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", NOALLOC_INVALID, ids=[c[0] for c in NOALLOC_INVALID])
+def test_noalloc_invalid_arguments_are_rejected_on_host(name, kw, status):
+    a = dict(q=A, k=B_, v=C, o=O, lse=L, B=1, H=2, S=128, D=64, scale=0.125, causal=0,
+             n_splits=2)
+    a.update(kw)
+    rc = _lib.attn_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                       a["S"], a["D"], a["scale"], a["causal"], a["n_splits"], 0)
+    assert _lib.STATUS_NAMES[rc] == status
+    assert _lib.load().attn_last_error().decode()
