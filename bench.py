@@ -48,7 +48,8 @@ def parse():
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the five-configuration timings, the sequence-length sweep "
-                         "(4k/8k/16k, B1 H8 D64) and the split-KV comparison")
+                         "(4k/8k/16k, B1 H8 D64), the split-KV comparison and the kernel "
+                         "variants")
     ap.add_argument("--sweep-steps", type=int, default=30,
                     help="timed launches per sweep point")
     ap.add_argument("--cold", action="store_true",
@@ -341,6 +342,52 @@ def run_splitkv(attn, dev, stream, steps, prewarm_ms):
     return out
 
 
+# Kernel variants timed against the default kernel: (workload, variant).
+VARIANT_BENCH = (("sdpa_b1h8s4096d64", 1), ("sdpa_b1h8s4096d64", 2), ("sdpa_b1h8s4096d64", 4),
+                 ("long_b1h8s16384d64", 1), ("long_b1h8s16384d64", 2),
+                 ("long_b1h8s16384d64", 4), ("causal_b2h16s8192d128", 2))
+VARIANT_NAMES = {1: "ring3", 2: "exp_poly", 4: "wide"}
+
+
+def run_variants(attn, dev, stream, steps, prewarm_ms):
+    """Kernel time of each compiled variant against the default kernel on the
+    same inputs, default first, each pre-warmed (attn_fwd_variant)."""
+    import torch
+
+    from testkit import WORKLOADS, workload_inputs
+
+    out = []
+    by_wl = {}
+    for name, var in VARIANT_BENCH:
+        by_wl.setdefault(name, []).append(var)
+    for name, variants in by_wl.items():
+        w = WORKLOADS[name]
+        q, k, v = (torch.from_numpy(x).to(dev) for x in workload_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+
+        def timed(fn):
+            prewarm(fn, prewarm_ms)
+            for _ in range(5):
+                fn()
+            durs, _ = time_launches(fn, stream, steps)
+            return float(durs.mean()) * 1e3
+
+        attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+        base_us = timed(raw_step("attn_fwd", q, k, v, o, lse, w, stream))
+        for var in variants:
+            attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream,
+                     variant=var)
+            us = timed(raw_step("attn_fwd_variant", q, k, v, o, lse, w, stream, extra=(var,)))
+            rec = {"workload": name, "variant": VARIANT_NAMES[var], "default_us": round(base_us, 3),
+                   "variant_us": round(us, 3), "variant_tflops": round(w.flops / (us * 1e-6) / 1e12, 2),
+                   "ratio": round(us / base_us, 4)}
+            log(f"variant {rec}")
+            out.append(rec)
+        del q, k, v, o, lse
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -452,6 +499,7 @@ def main():
         result["configs"] = run_configs(attn, dev, stream, args.sweep_steps, point_ms)
         result["sweep"] = run_sweep(attn, dev, stream, args.sweep_steps, point_ms)
         result["splitkv"] = run_splitkv(attn, dev, stream, args.sweep_steps, point_ms)
+        result["variants"] = run_variants(attn, dev, stream, args.sweep_steps, point_ms)
     if not args.no_cpu_baseline:
         log("CPU oracle leg ...")
         o_np = o.cpu().numpy()

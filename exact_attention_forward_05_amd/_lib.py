@@ -26,6 +26,10 @@ _SIGNATURES = [
      [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
       ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("attn_fwd_variant", ctypes.c_int,
+     [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+      ctypes.c_int, ctypes.c_void_p]),
     ("attn_fwd_splitkv_noalloc", ctypes.c_int,
      [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
@@ -73,6 +77,18 @@ def attn_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: in
     """Raw call of the C entry point with integer addresses; returns the status."""
     return load().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D,
                            ctypes.c_float(scale), causal, stream)
+
+
+# Kernel variants (ATTN_VARIANT_*) and the head dimensions each is built for.
+VARIANT_DEFAULT, VARIANT_RING3, VARIANT_EXP_POLY, VARIANT_WIDE = 0, 1, 2, 4
+VARIANTS = {64: (0, 1, 2, 4), 128: (0, 2)}
+
+
+def attn_fwd_variant(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
+                     S: int, D: int, scale: float, causal: int, variant: int, stream: int) -> int:
+    """Raw call of the variant entry point with integer addresses; returns the status."""
+    return load().attn_fwd_variant(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D,
+                                   ctypes.c_float(scale), causal, variant, stream)
 
 
 def attn_fwd_splitkv(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,

@@ -56,19 +56,26 @@ def _prepare(q, k, v, scale, out, lse, stream):
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
         causal: bool = False, out: Optional[torch.Tensor] = None,
         lse: Optional[torch.Tensor] = None,
-        stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+        stream: Optional[torch.cuda.Stream] = None,
+        variant: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Exact attention forward on the GPU.
 
     q, k, v: fp16 CUDA tensors of one shape [B, H, S, D], contiguous, D in {64, 128}.
     Returns (o, lse): o fp16 [B, H, S, D] and lse fp32 [B, H, S] (natural log).
     ``out``/``lse`` may be preallocated. The call is asynchronous on ``stream``
-    (default: torch's current stream).
+    (default: torch's current stream). ``variant`` selects a compiled kernel
+    variant (``_lib.VARIANT_*``; 0 is the default kernel).
     """
     B, H, S, D, scale, out, lse, stream = _prepare(q, k, v, scale, out, lse, stream)
     with torch.cuda.device(q.device):
-        st = _lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                           lse.data_ptr(), B, H, S, D, scale, int(bool(causal)),
-                           stream.cuda_stream)
+        if variant:
+            st = _lib.attn_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr(), B, H, S, D, scale, int(bool(causal)),
+                                       int(variant), stream.cuda_stream)
+        else:
+            st = _lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, H, S, D, scale, int(bool(causal)),
+                               stream.cuda_stream)
     _lib.check(st)
     return out, lse
 

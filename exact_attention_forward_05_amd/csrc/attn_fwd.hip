@@ -14,6 +14,9 @@
 
 static_assert(attn::BLOCK_M == attn::plan::BLOCK_M, "query tile of the kernel and of the plan");
 static_assert(attn::THREADS == attn::plan::THREADS, "workgroup size of the kernel and of the plan");
+static_assert(attn::VAR_RING3 == ATTN_VARIANT_RING3 && attn::VAR_EXP_POLY == ATTN_VARIANT_EXP_POLY &&
+                  attn::VAR_WIDE == ATTN_VARIANT_WIDE,
+              "variant flags of the kernel and of the header");
 
 namespace {
 
@@ -21,7 +24,7 @@ thread_local char g_last_error[512] = "";
 
 attn::plan::Msg msg() { return attn::plan::Msg{g_last_error, sizeof(g_last_error)}; }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int VAR = 0>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
            int S, float scale, int n_splits, void* workspace, hipStream_t stream) {
   using namespace attn;
@@ -38,10 +41,10 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   const _Float16* vh = static_cast<const _Float16*>(v);
   _Float16* oh = static_cast<_Float16*>(o);
   if (n_splits == 1) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false>), dim3((unsigned)L.blocks),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, VAR>), dim3((unsigned)L.blocks),
                        dim3(THREADS), 0, stream, qh, kh, vh, oh, lse, BH, S, L.n_qtiles, 1,
                        L.order, c, qsign, nullptr, nullptr);
-  } else {
+  } else if constexpr (VAR == 0) {
     float* part_o = static_cast<float*>(workspace);
     float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                plan::part_o_bytes(B, H, S, D, n_splits));
@@ -71,6 +74,40 @@ int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, i
                   : launch<64, false>(q, k, v, o, lse, B, H, S, scale, n_splits, workspace, st);
   return causal ? launch<128, true>(q, k, v, o, lse, B, H, S, scale, n_splits, workspace, st)
                 : launch<128, false>(q, k, v, o, lse, B, H, S, scale, n_splits, workspace, st);
+}
+
+// Single pass of a compiled kernel variant (attn::VAR_* flags), or
+// ATTN_ERR_UNSUPPORTED for a combination that is not built.
+template <int D, int VAR>
+int launch_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int S, float scale, int causal, hipStream_t st) {
+  return causal ? launch<D, true, VAR>(q, k, v, o, lse, B, H, S, scale, 1, nullptr, st)
+                : launch<D, false, VAR>(q, k, v, o, lse, B, H, S, scale, 1, nullptr, st);
+}
+
+int dispatch_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int S, int D, float scale, int causal, int variant, void* stream) {
+  using namespace attn;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (D == 64) {
+    switch (variant) {
+      case 0: return launch_variant<64, 0>(q, k, v, o, lse, B, H, S, scale, causal, st);
+      case VAR_RING3: return launch_variant<64, VAR_RING3>(q, k, v, o, lse, B, H, S, scale, causal, st);
+      case VAR_EXP_POLY: return launch_variant<64, VAR_EXP_POLY>(q, k, v, o, lse, B, H, S, scale, causal, st);
+      case VAR_WIDE: return launch_variant<64, VAR_WIDE>(q, k, v, o, lse, B, H, S, scale, causal, st);
+      default: break;
+    }
+  } else {
+    switch (variant) {
+      case 0: return launch_variant<128, 0>(q, k, v, o, lse, B, H, S, scale, causal, st);
+      case VAR_EXP_POLY: return launch_variant<128, VAR_EXP_POLY>(q, k, v, o, lse, B, H, S, scale, causal, st);
+      default: break;
+    }
+  }
+  return attn::plan::fail(msg(), ATTN_ERR_UNSUPPORTED,
+                          "kernel variant %d is not built for D=%d (D=64: 0, %d, %d, %d; "
+                          "D=128: 0, %d)", variant, D, ATTN_VARIANT_RING3, ATTN_VARIANT_EXP_POLY,
+                          ATTN_VARIANT_WIDE, ATTN_VARIANT_EXP_POLY);
 }
 
 int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -131,6 +168,14 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   const int rc = check_common(q, k, v, o, lse, B, H, S, D, scale, causal, 1);
   if (rc != ATTN_OK) return rc;
   return dispatch(q, k, v, o, lse, B, H, S, D, scale, causal, 1, nullptr, stream);
+}
+
+int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int S, int D, float scale, int causal, int variant, void* stream) {
+  g_last_error[0] = '\0';
+  const int rc = check_common(q, k, v, o, lse, B, H, S, D, scale, causal, 1);
+  if (rc != ATTN_OK) return rc;
+  return dispatch_variant(q, k, v, o, lse, B, H, S, D, scale, causal, variant, stream);
 }
 
 size_t attn_fwd_splitkv_workspace_size(int B, int H, int S, int D, int n_splits) {

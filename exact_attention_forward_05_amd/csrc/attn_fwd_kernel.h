@@ -9,15 +9,20 @@
 // translated from the page's mma.sync listings.
 //
 // Work decomposition. A workgroup of 8 waves owns BLOCK_M = 128 query rows of
-// one (batch, head). Waves 0-3 take 32 rows each and fold the even 64-key
-// tiles; waves 4-7 take the same rows and fold the odd tiles. The two waves on
-// one SIMD therefore work on independent data and can fill each other's
-// stalls. (gfx950 runs independent FMAs, exponentials and conversions beside
-// an MFMA stream, but the v_dot2 row sums wait for it, and the MFMA stream is
-// itself limited by its LDS operand reads; the interval order is chosen per
-// head dimension by measurement, see the schedule note at the kernel.) At the
-// end each odd-tile wave hands its carrier to its partner through LDS and the
-// two are merged.
+// one (batch, head) and streams the keys in intervals of 128, which arrive in
+// LDS as NPH tiles of BN = 128 / NPH keys. The waves form QGROUPS = 8 / NPH
+// query groups of 128 / QGROUPS rows; the NPH waves of a group take one tile
+// each per interval (wave phase p folds tiles p, p + NPH, ...), so the two
+// waves on one SIMD work on independent data and fill each other's stalls.
+//   D = 64:  NPH = 4, 32-key tiles, 2 query groups of 64 rows (4 sub-tiles of
+//            16 rows per wave);
+//   D = 128: NPH = 2, 64-key tiles, 4 query groups of 32 rows (2 sub-tiles).
+// Each K or V fragment read from LDS feeds the MFMAs of all of a wave's rows,
+// so at D = 64 the 64-row waves halve the operand reads per MFMA (the MFMA
+// stream was limited by them with 32-row waves); at D = 128 the output
+// accumulators of 64 rows would not fit next to the rest. At the end the NPH
+// carriers of a query group meet in LDS and each wave merges them for its
+// share of the output columns.
 //
 // MFMA: v_mfma_f32_16x16x32_f16. Lane l = 16*g + i (g = 0..3, i = 0..15):
 //   A: row i, contraction slots (g, 0..7); B: column i, slots (g, 0..7);
@@ -68,32 +73,48 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BLOCK_M = 128;          // query rows per workgroup
-constexpr int QGROUPS = 4;            // waves per key-tile parity (32 rows each)
-constexpr int WAVES = 2 * QGROUPS;    // even-tile and odd-tile waves
+constexpr int WAVES = 8;              // waves per workgroup, two per SIMD
 constexpr int THREADS = WAVES * 64;
-constexpr int QSUB = 2;               // 16-row query sub-tiles per wave
+constexpr int INTERVAL_KEYS = 128;    // keys per barrier interval
 constexpr float NEG_BIG = -1.0e30f;   // finite stand-in for -infinity
 // Lazy-max bound on a lane's tile sum: every probability stays below it, and
 // so below fp16's largest finite value (65504) with room for rounding.
 constexpr float P_LIMIT = 32768.0f;
 constexpr uint32_t BUF_FLAGS = 0x00020000u;  // raw buffer, 32-bit data format
 
-template <int D>
+// Compile-time variants of the kernel (bit flags), selectable through
+// attn_fwd_variant; 0 is the default kernel.
+enum : int {
+  VAR_RING3 = 1,     // D = 64: three-slot K/V ring, copies two intervals ahead
+  VAR_EXP_POLY = 2,  // one exponential in four by an FMA polynomial
+  VAR_WIDE = 4,      // D = 64: 64-row waves over four 32-key tiles per interval
+};
+
+template <int D, int VAR = 0>
 struct Geometry {
-  // Keys per tile: each wave folds one tile per barrier interval. (128-key
-  // tiles would spread the fixed per-interval costs further, but the larger
-  // score block does not fit the 256-register budget of two waves per SIMD.)
-  static constexpr int BN = 64;
+  // Key tiles per interval, one per wave of a query group (the wave's phase).
+  // 64-row waves at D = 64 (VAR_WIDE) halve the LDS operand reads per MFMA
+  // but measured no faster than 32-row waves (the path is not bound by
+  // them), so they are a variant.
+  static constexpr bool WIDE = D == 64 && (VAR & VAR_WIDE) != 0;
+  static constexpr int NPH = WIDE ? 4 : 2;
+  static constexpr int QGROUPS = WAVES / NPH;              // query groups
+  static constexpr int ROWS = BLOCK_M / QGROUPS;           // query rows per wave
+  static constexpr int QSUB = ROWS / 16;                   // 16-row query sub-tiles per wave
+  // Keys per tile: each wave folds one tile per barrier interval. (At D = 64,
+  // 64-row waves with 64-key tiles would not fit the 256-register budget of
+  // two waves per SIMD; nor would 128-key tiles with 32-row waves.)
+  static constexpr int BN = INTERVAL_KEYS / NPH;
   static constexpr int KB = BN / 16;                       // 16-key MFMA blocks of S^T
   static constexpr int KC = BN / 32;                       // 32-key chunks of the P.V contraction
   static constexpr int K_HALVES = BN * D;                  // K rows unpadded, swizzled
   static constexpr int V_HALVES = BN * D;                  // V rows unpadded, swizzled
-  // Two-slot rings of tile pairs (even tile for the even waves, odd tile for
-  // the odd waves) for K and for V: one pair is read while the next is
-  // copied. (Deeper rings, and two pairs per barrier interval, measured no
-  // faster.)
-  static constexpr int RING = 2;
-  static constexpr int SLOT_HALVES = 2 * K_HALVES;          // one tile pair
+  // Two-slot rings of tile groups (one tile per phase) for K and for V: one
+  // group is read while the next is copied. A three-slot ring (VAR_RING3,
+  // D = 64 only: at D = 128 it does not fit next to the Q tile) runs the
+  // copies two intervals ahead; it measured no faster.
+  static constexpr int RING = (D == 64 && (VAR & VAR_RING3) != 0) ? 3 : 2;
+  static constexpr int SLOT_HALVES = NPH * K_HALVES;        // one interval's tiles
   // At D = 128 the Q fragments would not fit the register budget next to the
   // output accumulators: the workgroup's Q rows are staged in LDS instead.
   static constexpr bool Q_IN_LDS = D == 128;
@@ -112,19 +133,30 @@ struct Geometry {
   // SIMD's other wave, in its MFMA phase or later in its own softmax, does not
   // starve it (2-3% on every workload).
   static constexpr bool SOFTMAX_PRIO = true;
+  // One exponential in four computed on the FMA path (VAR_EXP_POLY).
+  static constexpr bool EXP_POLY = (VAR & VAR_EXP_POLY) != 0;
   static constexpr int Q_HALVES = Q_IN_LDS ? BLOCK_M * D : 0;
-  static constexpr int LDS_HALVES = 2 * RING * SLOT_HALVES + Q_HALVES;
-  static constexpr int LDS_BYTES = LDS_HALVES * 2;
   static constexpr int D_CHUNKS = D / 32;                  // contraction chunks of Q.K
   static constexpr int D_BLOCKS = D / 16;                  // 16-row blocks of O^T
-  // per tile pair, K and V each in 16-byte pieces
-  static constexpr int PIECES = 2 * BN * (D / 8);
+  // per interval, K and V each in 16-byte pieces
+  static constexpr int PIECES = NPH * BN * (D / 8);
   static constexpr int LOADS = PIECES / THREADS;
   static_assert(D % 64 == 0, "D must be a multiple of 64");
   static_assert(LOADS * THREADS == PIECES, "tiling");
-  // carrier hand-off area (after the key loop): per odd wave, per lane
-  static constexpr int CARRIER_FLOATS = QSUB * (2 + 4 * D_BLOCKS);
-  static_assert(QGROUPS * 64 * CARRIER_FLOATS * 4 <= LDS_BYTES, "hand-off fits in LDS");
+  static_assert(QSUB * 16 * QGROUPS == BLOCK_M && KB >= 2 && KC >= 1, "geometry");
+  // Carrier hand-off (after the key loop): each wave finalises OWN_DB of the
+  // output's 16-column blocks for its rows. Per wave, 16-byte slots of 64
+  // lanes: {m, d} of two sub-tiles per slot, then one slot per sub-tile and
+  // output block.
+  static constexpr int OWN_DB = D_BLOCKS / NPH;
+  static constexpr int MD_SLOTS = (QSUB + 1) / 2;
+  static constexpr int HANDOFF_SLOTS = MD_SLOTS + QSUB * D_BLOCKS;
+  static constexpr int HANDOFF_BYTES = WAVES * HANDOFF_SLOTS * 64 * 16;
+  static constexpr int LOOP_BYTES = (2 * RING * SLOT_HALVES + Q_HALVES) * 2;
+  static constexpr int LDS_BYTES = LOOP_BYTES > HANDOFF_BYTES ? LOOP_BYTES : HANDOFF_BYTES;
+  static constexpr int LDS_HALVES = LDS_BYTES / 2;
+  static_assert(OWN_DB * NPH == D_BLOCKS, "output blocks split over a query group");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -180,11 +212,11 @@ __device__ __forceinline__ int v_swizzle(int r) {
   return 2 * ((r & 3) + 4 * ((r >> 3) & 1));
 }
 
-// Direct global->LDS copy of one tile pair. A buffer load with the LDS flag
-// writes lane l's 16 bytes at M0 + 16*l, so each wave instruction fills 1 KB
-// of LDS in slot order; each lane therefore fetches the global piece that
+// Direct global->LDS copy of one interval's tiles. A buffer load with the LDS
+// flag writes lane l's 16 bytes at M0 + 16*l, so each wave instruction fills
+// 1 KB of LDS in slot order; each lane therefore fetches the global piece that
 // belongs in its slot. Per-lane byte offsets (relative to the first key of the
-// pair) are precomputed for K and for V.
+// interval) are precomputed for K and for V.
 template <int D>
 struct CopyPlan {
   uint32_t k_off[Geometry<D>::LOADS];
@@ -193,7 +225,7 @@ struct CopyPlan {
 
 template <int D>
 __device__ __forceinline__ int copy_unit(int wave, int i) {
-  return i * WAVES + wave;  // 1 KB unit of the pair filled by instruction i of a wave
+  return i * WAVES + wave;  // 1 KB unit of the slot filled by instruction i of a wave
 }
 
 template <int D>
@@ -204,7 +236,7 @@ __device__ __forceinline__ void make_copy_plan(CopyPlan<D>& cp, int wave, int la
 #pragma unroll
   for (int i = 0; i < Geometry<D>::LOADS; ++i) {
     const int slot = copy_unit<D>(wave, i) * 64 + lane;
-    const int t = slot / TILE_SLOTS;                // tile of the pair
+    const int t = slot / TILE_SLOTS;                // tile of the interval
     const int w = slot % TILE_SLOTS;
     const int row = w / CHUNKS;
     const int pc = w % CHUNKS;                       // physical chunk in the row
@@ -222,10 +254,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t keys_from(const _Float16* base
   return make_rsrc(base + (int64_t)key0 * D, bytes);
 }
 
-// Issue the direct copy of the tile pair starting at key0 into `slot` (the
-// pair's LDS area: tile 0 then tile 1). Completion is awaited with vmcnt.
+// Issue the direct copy of the interval starting at key0 into `slot` (its LDS
+// area: tile 0, tile 1, ...). Completion is awaited with vmcnt.
 template <int D>
-__device__ __forceinline__ void copy_pair(const uint32_t* off, const _Float16* base, int key0,
+__device__ __forceinline__ void copy_group(const uint32_t* off, const _Float16* base, int key0,
                                           int S, _Float16* slot, int wave) {
   const __amdgpu_buffer_rsrc_t rs = keys_from<D>(base, key0, S);
 #pragma unroll
@@ -238,6 +270,14 @@ __device__ __forceinline__ void copy_pair(const uint32_t* off, const _Float16* b
 
 // Wait until this wave's direct copies (vector memory operations) are done.
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector memory operations are in flight
+// (they complete in order): the N most recent copies may still run.
+template <int N>
+__device__ __forceinline__ void wait_copies_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt encoding (gfx9): vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // LDS transposing read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane n supplies the address of 4 consecutive halves X[n][0..3]; lane n
@@ -257,6 +297,17 @@ struct Carrier {
   float d;                         // this lane's share of the denominator
 };
 
+// Per-wave register sets: carriers and Q^T fragments of the QSUB sub-tiles, a
+// tile's scores, and its fp16 probabilities.
+template <int D, int VAR>
+using CarrierSet = Carrier<D>[Geometry<D, VAR>::QSUB];
+template <int D, int VAR>
+using QSet = f16x8[Geometry<D, VAR>::QSUB][Geometry<D, VAR>::D_CHUNKS];
+template <int D, int VAR>
+using ScoreSet = f32x4[Geometry<D, VAR>::QSUB][Geometry<D, VAR>::KB];
+template <int D, int VAR>
+using ProbSet = f16x8[Geometry<D, VAR>::QSUB][Geometry<D, VAR>::KC];
+
 // Scheduling groups (sched_group_barrier masks): LDS reads and MFMAs.
 constexpr int SG_DS_READ = 0x100;
 constexpr int SG_MFMA = 0x008;
@@ -269,13 +320,13 @@ __device__ __forceinline__ void pin_reads() {
     pin_reads<U + 1, END, NPV>();
   }
 }
-template <int U, int NU, int NPV, int AHEAD>
+template <int U, int NU, int NPV, int AHEAD, int QSUB>
 __device__ __forceinline__ void pin_units() {
   if constexpr (U < NU) {
     if constexpr (U + AHEAD < NU)
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, U + AHEAD < NPV ? 2 : 1, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, QSUB, 0);
-    pin_units<U + 1, NU, NPV, AHEAD>();
+    pin_units<U + 1, NU, NPV, AHEAD, QSUB>();
   }
 }
 
@@ -285,21 +336,23 @@ __device__ __forceinline__ void pin_units() {
 // read for K) and the two MFMAs (both query sub-tiles) that consume it.
 // Fragments are read AHEAD units before use, so the LDS latency is covered by
 // the MFMAs in between. Units are ordered so that consecutive MFMAs on one
-// accumulator are several instructions apart.
-template <int D, bool PV, bool QK>
-__device__ __forceinline__ void mfma_phase(Carrier<D> (&cr)[QSUB],
-                                           const f16x8 (&pf)[QSUB][Geometry<D>::KC],
-                                           f32x4 (&sc)[QSUB][Geometry<D>::KB],
-                                           const f16x8 (&qf)[QSUB][Geometry<D>::D_CHUNKS],
+// accumulator are several instructions apart (QSUB MFMAs per unit).
+template <int D, int VAR, bool PV, bool QK>
+__device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
+                                           const ProbSet<D, VAR>& pf,
+                                           ScoreSet<D, VAR>& sc,
+                                           const QSet<D, VAR>& qf,
                                            const _Float16* __restrict__ vtile,
                                            const _Float16* __restrict__ ktile,
                                            const _Float16* __restrict__ qtile, uint32_t qsign,
                                            int li, int g) {
-  using G = Geometry<D>;
+  using G = Geometry<D, VAR>;
+  constexpr int QSUB = G::QSUB;
   constexpr int NPV = PV ? G::KC * G::D_BLOCKS : 0;
   constexpr int NQK = QK ? G::KB * G::D_CHUNKS : 0;
   constexpr int NU = NPV + NQK;
-  constexpr int AHEAD = (D == 64 ? 8 : 4) < NU ? (D == 64 ? 8 : 4) : NU;
+  constexpr int AHEAD_MAX = D == 64 ? 8 : 4;
+  constexpr int AHEAD = AHEAD_MAX < NU ? AHEAD_MAX : NU;
   // V^T operand (d block db, key chunk kc): lane (i, g) needs
   // V[32kc + 8g + e][16db + i], e = 0..7 -- two transposing reads over 4 key
   // rows x 16 d, source lane n of group g pointing at row 32kc + 8g + 4h + n/4,
@@ -371,17 +424,39 @@ __device__ __forceinline__ void mfma_phase(Carrier<D> (&cr)[QSUB],
   // then per unit the reads of unit u + AHEAD followed by unit u's two MFMAs.
   if constexpr (D == 64) {
     pin_reads<0, AHEAD, NPV>();
-    pin_units<0, NU, NPV, AHEAD>();
+    pin_units<0, NU, NPV, AHEAD, QSUB>();
   }
 }
 
-// exp2(t - m) of a 4-score accumulator, hidden keys forced to 0 when MASK.
-template <bool MASK>
+// 2^x on the FMA path (the exponential offload of the VAR_EXP_POLY variant,
+// after FlashAttention-4's emulated exponential; the coefficients are this
+// project's own fit). x is clamped to [-126, 127]: arguments above still
+// overflow fp16 after conversion (so the lazy-max test sees them) and those
+// below vanish, and the exponent-field add below cannot reach the sign bit.
+// n = floor(x), f = x - n in [0, 1), 2^f by the degree-3 polynomial that
+// minimises the largest relative error on [0, 1] (Remez exchange,
+// csrc/fit_exp2_poly.py: 7.5e-5, below the fp16 rounding of P), and 2^n
+// applied by adding n to the exponent field. Eight VALU instructions against
+// one v_exp_f32.
+__device__ __forceinline__ float exp2_poly(float x) {
+  constexpr float C0 = 9.999251962e-01f, C1 = 6.958335638e-01f, C2 = 2.260671556e-01f,
+                  C3 = 7.802452147e-02f;
+  x = __builtin_amdgcn_fmed3f(x, -126.0f, 127.0f);
+  const float fl = __builtin_floorf(x);
+  const float f = x - fl;
+  const float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(C3, f, C2), f, C1), f, C0);
+  return __uint_as_float(__float_as_uint(p) + ((uint32_t)(int)fl << 23));
+}
+
+// exp2(t - m) of a 4-score accumulator, hidden keys forced to 0 when MASK;
+// with POLY the last of the four on the FMA path.
+template <bool MASK, bool POLY>
 __device__ __forceinline__ f32x4 exp_block(f32x4 s, float c, float m, uint32_t hid) {
   f32x4 p;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m));
+    const float t = __builtin_fmaf(s[r], c, -m);
+    float e = POLY && r == 3 ? exp2_poly(t) : __builtin_amdgcn_exp2f(t);
     if (MASK) e = ((hid >> r) & 1u) ? 0.0f : e;
     p[r] = e;
   }
@@ -390,12 +465,13 @@ __device__ __forceinline__ f32x4 exp_block(f32x4 s, float c, float m, uint32_t h
 
 // Online softmax of one tile's scores: probabilities (fp16, P^T operand
 // layout) into pf, denominators and, when the max moves, outputs rescaled.
-template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB],
-                                             const f32x4 (&sc)[QSUB][Geometry<D>::KB],
-                                             f16x8 (&pf)[QSUB][Geometry<D>::KC], float c, int key0,
+template <int D, int VAR, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
+                                             const ScoreSet<D, VAR>& sc,
+                                             ProbSet<D, VAR>& pf, float c, int key0,
                                              int qrow0, int S, int li, int g) {
-  using G = Geometry<D>;
+  using G = Geometry<D, VAR>;
+  constexpr int QSUB = G::QSUB;
   // hidden-key bits per sub-tile and key block (bit r: accumulator element r)
   uint32_t hid[QSUB][G::KB];
 #pragma unroll
@@ -424,7 +500,7 @@ __device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB],
     const float m = cr[qs].m;
     f32x4 p[G::KB];
 #pragma unroll
-    for (int kb = 0; kb < G::KB; ++kb) p[kb] = exp_block<MASK>(sc[qs][kb], c, m, hid[qs][kb]);
+    for (int kb = 0; kb < G::KB; ++kb) p[kb] = exp_block<MASK, G::EXP_POLY>(sc[qs][kb], c, m, hid[qs][kb]);
     float acc[2] = {SUM_ONTO_D ? cr[qs].d : 0.0f, 0.0f};
 #pragma unroll
     for (int kc = 0; kc < G::KC; ++kc) {
@@ -487,44 +563,47 @@ __device__ __forceinline__ void softmax_tile(Carrier<D> (&cr)[QSUB],
   for (int qs = 0; qs < QSUB; ++qs) cr[qs].d = SUM_ONTO_D ? dnew[qs] : cr[qs].d + tsum[qs];
 }
 
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void softmax_any(Carrier<D> (&cr)[QSUB],
-                                            const f32x4 (&sc)[QSUB][Geometry<D>::KB],
-                                            f16x8 (&pf)[QSUB][Geometry<D>::KC], float c, int key0,
+template <int D, int VAR, bool CAUSAL>
+__device__ __forceinline__ void softmax_any(CarrierSet<D, VAR>& cr,
+                                            const ScoreSet<D, VAR>& sc,
+                                            ProbSet<D, VAR>& pf, float c, int key0,
                                             int qrow0, int S, int li, int g) {
-  constexpr int BN = Geometry<D>::BN;
+  constexpr int BN = Geometry<D, VAR>::BN;
   // Element masks are needed on the sequence tail and on tiles reaching past
   // the wave's first query (causal diagonal).
   const bool needs_mask = (key0 + BN > S) || (CAUSAL && key0 + BN - 1 > qrow0);
   if (needs_mask)
-    softmax_tile<D, CAUSAL, true>(cr, sc, pf, c, key0, qrow0, S, li, g);
+    softmax_tile<D, VAR, CAUSAL, true>(cr, sc, pf, c, key0, qrow0, S, li, g);
   else
-    softmax_tile<D, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
+    softmax_tile<D, VAR, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
 }
 
 // Workgroup id -> (batch*head, query tiles) by `order` (work_order.h).
 //
-// Schedule. Key tiles come in pairs (2p, 2p+1): even waves fold tile 2p and
-// odd waves tile 2p+1, one pair per barrier interval, with K and V copied
-// into LDS during the interval before they are read.
-//  D = 64: interval j is Q.K^T of pair j, the softmax, then P.V of pair j.
-//  D = 128: interval j is an MFMA phase (P.V of pair j-1, Q.K^T of pair j)
-//    and the softmax of pair j; odd waves take the two halves in the other
-//    order (softmax of pair j-1 first), so that on each SIMD one wave's
-//    softmax runs against the other's MFMA phase.
+// Schedule. Key interval j holds tiles NPH*j .. NPH*j + NPH - 1; the wave of
+// phase p folds tile NPH*j + p, with K and V copied into LDS during the
+// interval before they are read.
+//  D = 64: interval j is Q.K^T of tile j, the softmax, then P.V of tile j.
+//  D = 128: interval j is an MFMA phase (P.V of interval j-1, Q.K^T of
+//    interval j) and the softmax of interval j; the second wave of each SIMD
+//    (waves 4-7) takes the two halves in the other order (softmax of interval
+//    j-1 first), so that one wave's softmax runs against the other's MFMA
+//    phase.
 //
 // SPLIT: the key range of each query tile is cut into n_splits runs of whole
-// tile pairs (split-KV). Workgroup (query tile, head, split) folds its run
-// and stores the partial result -- o/d in fp32 and m + log2(d) -- into the
+// intervals (split-KV). Workgroup (query tile, head, split) folds its run and
+// stores the partial result -- o/d in fp32 and m + log2(d) -- into the
 // workspace instead of O and LSE; attn_combine_kernel merges the runs.
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, bool SPLIT, int VAR = 0>
 __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
     int BH, int S, int n_qtiles, int n_splits, int order, float c, uint32_t qsign,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
-  using G = Geometry<D>;
+  using G = Geometry<D, VAR>;
   constexpr int R = G::RING;
+  constexpr int QSUB = G::QSUB;
+  constexpr int NPH = G::NPH;
   __shared__ __attribute__((aligned(16))) _Float16 smem[G::LDS_HALVES];
   _Float16* kring = smem;                           // [slot][tile] K tiles
   _Float16* vring = smem + R * G::SLOT_HALVES;      // [slot][tile] V tiles
@@ -539,8 +618,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   const _Float16* kh = k + head;
   const _Float16* vh = v + head;
 
-  // One query tile: Q load, the key loop and the epilogue. Odd-tile waves
-  // leave it after handing over their carriers.
+  // One query tile: Q load, the key loop and the epilogue.
   auto run_tile = [&](const int qt) __attribute__((always_inline)) {
     // Lane indices are derived afresh for each tile (the empty asm hides
     // the thread id from the optimiser), so that nothing lane-dependent is
@@ -551,10 +629,11 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const int lane = tid & 63;
     const int li = lane & 15;
     const int g = lane >> 4;
-    const int qgrp = wave % QGROUPS;
-    const int parity = wave / QGROUPS;
+    const int qgrp = wave % G::QGROUPS;
+    const int phase = wave / G::QGROUPS;
+    const bool late = wave >= WAVES / 2;  // second wave of its SIMD
     const int q0 = qt * BLOCK_M;
-    const int qrow0 = q0 + 32 * qgrp;  // this wave's first query row
+    const int qrow0 = q0 + G::ROWS * qgrp;  // this wave's first query row
 
     // Q^T fragments, loaded once (sign-flipped when the scale is negative):
     // into registers, or (Q_IN_LDS) the workgroup's Q rows into LDS by direct
@@ -588,7 +667,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
         }
       }
     }
-    const _Float16* qwave = qtile + 32 * qgrp * D;  // this wave's rows in the LDS Q tile
+    const _Float16* qwave = qtile + G::ROWS * qgrp * D;  // this wave's rows in the LDS Q tile
 
     Carrier<D> cr[QSUB];
   #pragma unroll
@@ -606,213 +685,288 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
 
     const int kend = CAUSAL ? min(S, q0 + BLOCK_M) : S;
     const int n_kt = (kend + G::BN - 1) / G::BN;
-    const int n_pairs_all = (n_kt + 1) / 2;
-    // This workgroup folds tile pairs [pb, pb + n_pairs): all of them, or its
+    const int n_int_all = (n_kt + NPH - 1) / NPH;
+    // This workgroup folds intervals [pb, pb + n_int): all of them, or its
     // split's run.
-    const int pb = SPLIT ? (int)((int64_t)split * n_pairs_all / n_splits) : 0;
-    const int n_pairs = SPLIT ? (int)((int64_t)(split + 1) * n_pairs_all / n_splits) - pb : n_pairs_all;
-    // Pairs whose tile of this wave's parity holds keys for its rows: a prefix,
-    // since tiles past S or past the wave's last query (causal) are skipped.
-    const int row_end = CAUSAL ? min(kend, qrow0 + 32) : kend;  // keys < row_end are needed
+    const int pb = SPLIT ? (int)((int64_t)split * n_int_all / n_splits) : 0;
+    const int n_int = SPLIT ? (int)((int64_t)(split + 1) * n_int_all / n_splits) - pb : n_int_all;
+    // Intervals whose tile of this wave's phase holds keys for its rows: a
+    // prefix, since tiles past S or past the wave's last query (causal) are
+    // skipped.
+    const int row_end = CAUSAL ? min(kend, qrow0 + G::ROWS) : kend;  // keys < row_end are needed
     const int live_tiles = (row_end + G::BN - 1) / G::BN;
-    const int n_live = min(max((live_tiles - parity + 1) / 2 - pb, 0), n_pairs);
+    const int n_live = min(max((live_tiles - phase + NPH - 1) / NPH - pb, 0), n_int);
     constexpr bool PINGPONG = G::PINGPONG;
-    // Only the last live pair of a wave can need element masks: the sequence
-    // tail is in the last tile, and a tile crossing the causal diagonal of the
-    // wave's 32 rows is the last one at or below them. (The last live pair of
-    // a split run is checked at run time.)
+    // Only the last live interval of a wave can need element masks: the
+    // sequence tail is in the last tile, and the tiles crossing the causal
+    // diagonal of the wave's rows are the last ones at or below them, which
+    // fall to different phases. (The last live interval of a split run is
+    // checked at run time.)
 
     CopyPlan<D> cp;
     make_copy_plan<D>(cp, wave, lane);
-    if (n_pairs > 0) copy_pair<D>(cp.k_off, kh, 2 * pb * G::BN, S, kring, wave);  // K of pair pb
+    if (n_int > 0) copy_group<D>(cp.k_off, kh, pb * INTERVAL_KEYS, S, kring, wave);  // K of interval pb
     if constexpr (G::PV_SAME) {
-      if (n_pairs > 0) copy_pair<D>(cp.v_off, vh, 2 * pb * G::BN, S, vring, wave);  // V of pair pb
+      if (n_int > 0) copy_group<D>(cp.v_off, vh, pb * INTERVAL_KEYS, S, vring, wave);  // V of interval pb
     }
-    wait_copies();
+    if constexpr (G::PV_SAME && R == 3) {
+      // three-slot ring: interval pb + 1 is in flight from the start
+      if (n_int > 1) {
+        copy_group<D>(cp.k_off, kh, (pb + 1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, wave);
+        copy_group<D>(cp.v_off, vh, (pb + 1) * INTERVAL_KEYS, S, vring + G::SLOT_HALVES, wave);
+        wait_copies_keep<2 * G::LOADS>();
+      } else {
+        wait_copies();
+      }
+    } else {
+      wait_copies();
+    }
     __syncthreads();
 
-    // Two-phase order (D = 128), barrier interval j (pairs counted from pb):
-    // P.V of pair j-1 and Q.K^T of pair j (MFMA), then the copies of K of pair
-    // j+1 and V of pair j, then the softmax of pair j (VALU); the
-    // probabilities stay in registers for interval j+1. The copies sit between
-    // the MFMA phase (whose LDS reads they would slow) and the softmax (which
-    // does not touch LDS). K of pair j is read from ring slot j % 2 and V of
-    // pair j-1 from slot (j-1) % 2, both copied in interval j-1. Every wave
-    // runs all n_pairs + 1 intervals; the bodies are specialised (compile-time
-    // flags) so that the steady state has no branches.
+    // Two-phase order (D = 128), barrier interval j (counted from pb): P.V of
+    // interval j-1 and Q.K^T of interval j (MFMA), then the copies of K of
+    // interval j+1 and V of interval j, then the softmax of interval j
+    // (VALU); the probabilities stay in registers for interval j+1. The
+    // copies sit between the MFMA phase (whose LDS reads they would slow) and
+    // the softmax (which does not touch LDS). K of interval j is read from
+    // ring slot j % 2 and V of interval j-1 from slot (j-1) % 2, both copied
+    // in interval j-1. Every wave runs all n_int + 1 intervals; the bodies
+    // are specialised (compile-time flags) so that the steady state has no
+    // branches.
     auto copies = [&](int j) __attribute__((always_inline)) {
-      if (j + 1 < n_pairs)
-        copy_pair<D>(cp.k_off, kh, 2 * (pb + j + 1) * G::BN, S,
-                     kring + ((j + 1) & 1) * G::SLOT_HALVES, wave);
-      if (j < n_pairs)
-        copy_pair<D>(cp.v_off, vh, 2 * (pb + j) * G::BN, S, vring + (j & 1) * G::SLOT_HALVES, wave);
+      if (j + 1 < n_int)
+        copy_group<D>(cp.k_off, kh, (pb + j + 1) * INTERVAL_KEYS, S,
+                      kring + ((j + 1) & 1) * G::SLOT_HALVES, wave);
+      if (j < n_int)
+        copy_group<D>(cp.v_off, vh, (pb + j) * INTERVAL_KEYS, S,
+                      vring + (j & 1) * G::SLOT_HALVES, wave);
     };
-    // softmax of pair p of this wave's parity (masks possible when EDGE)
-    auto softmax_pair = [&](int p, auto edge_flag) __attribute__((always_inline)) {
+    // softmax of this wave's tile of interval p (masks possible when EDGE)
+    auto softmax_int = [&](int p, auto edge_flag) __attribute__((always_inline)) {
       if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(2);
-      const int key0 = (2 * (pb + p) + parity) * G::BN;
+      const int key0 = (pb + p) * INTERVAL_KEYS + phase * G::BN;
       if constexpr (decltype(edge_flag)::value)
-        softmax_any<D, CAUSAL>(cr, sc, pf, c, key0, qrow0, S, li, g);
+        softmax_any<D, VAR, CAUSAL>(cr, sc, pf, c, key0, qrow0, S, li, g);
       else
-        softmax_tile<D, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
+        softmax_tile<D, VAR, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
       if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(0);
     };
     auto mfma = [&](int j, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
       constexpr bool PV = decltype(pv_flag)::value;
       constexpr bool QK = decltype(qk_flag)::value;
-      const _Float16* kslot = kring + (j & 1) * G::SLOT_HALVES + parity * G::K_HALVES;
-      const _Float16* vslot = vring + ((j + 1) & 1) * G::SLOT_HALVES + parity * G::V_HALVES;
-      if constexpr (PV || QK) mfma_phase<D, PV, QK>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+      const _Float16* kslot = kring + (j & 1) * G::SLOT_HALVES + phase * G::K_HALVES;
+      const _Float16* vslot = vring + ((j + 1) & 1) * G::SLOT_HALVES + phase * G::V_HALVES;
+      if constexpr (PV || QK) mfma_phase<D, VAR, PV, QK>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
     };
     auto end_interval = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
       wait_copies();
       __syncthreads();
     };
-    // Even waves: MFMA phase, copies, softmax of the pair just scored.
-    auto even_interval = [&](int j, auto pv_flag, auto qk_flag, auto edge_flag) __attribute__((always_inline)) {
-      mfma(j, pv_flag, qk_flag);
-      __builtin_amdgcn_sched_barrier(0);
-      copies(j);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (decltype(qk_flag)::value) softmax_pair(j, edge_flag);
-      end_interval();
-    };
-    // Odd waves run the same work half an interval out of phase: the softmax of
-    // the pair scored in the previous interval, copies, then the MFMA phase. On
-    // each SIMD one wave's softmax thus overlaps the other's MFMA phase.
-    auto odd_interval = [&](int j, auto sm_flag, auto edge_flag, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
-      if constexpr (decltype(sm_flag)::value) softmax_pair(j - 1, edge_flag);
-      __builtin_amdgcn_sched_barrier(0);
-      copies(j);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma(j, pv_flag, qk_flag);
-      end_interval();
-    };
     using T_ = std::true_type;
     using F_ = std::false_type;
     int j = 0;
     if constexpr (G::PV_SAME) {
-      // Three-phase order (D = 64), interval j: Q.K^T of pair j, copies of K
-      // and V of pair j+1 (into the slots of pair j-1, read in interval j-1),
-      // softmax of pair j, P.V of pair j. Every wave runs n_pairs intervals.
-      auto copies_next = [&](int jj) __attribute__((always_inline)) {
-        if (jj + 1 < n_pairs) {
-          copy_pair<D>(cp.k_off, kh, 2 * (pb + jj + 1) * G::BN, S,
-                       kring + ((jj + 1) & 1) * G::SLOT_HALVES, wave);
-          copy_pair<D>(cp.v_off, vh, 2 * (pb + jj + 1) * G::BN, S,
-                       vring + ((jj + 1) & 1) * G::SLOT_HALVES, wave);
+      // Three-phase order (D = 64), interval j: Q.K^T of interval j, copies of
+      // K and V of interval j + R - 1 (into the slot of interval j-1, read in
+      // interval j-1), softmax of interval j, P.V of interval j. Every wave
+      // runs n_int intervals. With a three-slot ring the copies run two
+      // intervals ahead of their use, so their latency (about as long as an
+      // interval) is off the barrier's critical path.
+      constexpr int AH = R - 1;  // intervals between a copy and its use
+      auto copies_ahead = [&](int jj) __attribute__((always_inline)) {
+        if (jj + AH < n_int) {
+          const int sl = (jj + AH) % R;
+          copy_group<D>(cp.k_off, kh, (pb + jj + AH) * INTERVAL_KEYS, S,
+                        kring + sl * G::SLOT_HALVES, wave);
+          copy_group<D>(cp.v_off, vh, (pb + jj + AH) * INTERVAL_KEYS, S,
+                        vring + sl * G::SLOT_HALVES, wave);
         }
       };
-      // slot_flag: the ring slot of pair jj as a compile-time constant, or
-      // -1 to take it from jj at run time.
+      // End of interval jj: the copies of interval jj + 1 must have landed
+      // (those of jj + 2, issued in this interval, may still run).
+      auto end_int = [&](int jj) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (R > 2 && jj + AH < n_int)
+          wait_copies_keep<2 * G::LOADS>();
+        else
+          wait_copies();
+        __syncthreads();
+      };
+      // slot_flag: the ring slot of interval jj as a compile-time constant,
+      // or -1 to take it from jj at run time.
       auto full = [&](int jj, auto edge_flag, auto slot_flag) __attribute__((always_inline)) {
         constexpr int SL = decltype(slot_flag)::value;
-        const int slot = SL >= 0 ? SL : (jj & 1);
-        const _Float16* kslot = kring + slot * G::SLOT_HALVES + parity * G::K_HALVES;
-        const _Float16* vslot = vring + slot * G::SLOT_HALVES + parity * G::V_HALVES;
-        mfma_phase<D, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+        const int slot = SL >= 0 ? SL : jj % R;
+        const _Float16* kslot = kring + slot * G::SLOT_HALVES + phase * G::K_HALVES;
+        const _Float16* vslot = vring + slot * G::SLOT_HALVES + phase * G::V_HALVES;
+        mfma_phase<D, VAR, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
         __builtin_amdgcn_sched_barrier(0);
-        copies_next(jj);
+        copies_ahead(jj);
         __builtin_amdgcn_sched_barrier(0);
-        softmax_pair(jj, edge_flag);
+        softmax_int(jj, edge_flag);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_phase<D, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
-        end_interval();
+        mfma_phase<D, VAR, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+        end_int(jj);
       };
       using S0 = std::integral_constant<int, 0>;
       using S1 = std::integral_constant<int, 1>;
+      using S2 = std::integral_constant<int, 2>;
       using SR = std::integral_constant<int, -1>;
-      // Steady state unrolled by two, so that the ring slots are constant
-      // offsets of the LDS reads rather than addresses computed per interval.
-      for (; j + 2 < n_live; j += 2) {
-        full(j, F_{}, S0{});
-        full(j + 1, F_{}, S1{});
+      // Steady state unrolled by the ring depth, so that the ring slots are
+      // constant offsets of the LDS reads rather than addresses computed per
+      // interval.
+      if constexpr (R == 3) {
+        for (; j + 3 < n_live; j += 3) {
+          full(j, F_{}, S0{});
+          full(j + 1, F_{}, S1{});
+          full(j + 2, F_{}, S2{});
+        }
+        for (; j + 1 < n_live; ++j) full(j, F_{}, SR{});
+      } else {
+        for (; j + 2 < n_live; j += 2) {
+          full(j, F_{}, S0{});
+          full(j + 1, F_{}, S1{});
+        }
+        if (j + 1 < n_live) full(j++, F_{}, S0{});  // j is even here
       }
-      if (j + 1 < n_live) full(j++, F_{}, S0{});  // j is even here
       if (j + 1 == n_live) full(j++, T_{}, SR{});
-      for (; j < n_pairs; ++j) {
-        copies_next(j);
-        end_interval();
+      for (; j < n_int; ++j) {
+        copies_ahead(j);
+        end_int(j);
       }
-    } else if (parity == 0 || !PINGPONG) {
-      if (n_live >= 1)
-        even_interval(j++, F_{}, T_{}, T_{});
-      else
-        even_interval(j++, F_{}, F_{}, F_{});
-      for (; j + 1 < n_live; ++j) even_interval(j, T_{}, T_{}, F_{});  // steady state
-      if (j + 1 == n_live) even_interval(j++, T_{}, T_{}, T_{});       // last live pair
-      if (j == n_live && j >= 1) even_interval(j++, T_{}, F_{}, F_{}); // its P.V
-      for (; j <= n_pairs; ++j) even_interval(j, F_{}, F_{}, F_{});    // idle: copies, barriers
     } else {
-      // flags: softmax of the previous pair, its masks, P.V, Q.K^T
+      // Two-phase order as one instruction stream for every wave: interval
+      // body j is the MFMA phase (P.V of j-1, Q.K^T of j), then the softmax
+      // of j. The first wave of each SIMD ends its interval after the
+      // softmax; with PINGPONG the second wave (waves 4-7) ends it right after
+      // the MFMA phase, so between two barriers it runs the softmax of j-1
+      // and then the MFMA phase of j while its partner runs the MFMA phase
+      // and then the softmax of j: one wave's softmax overlaps the other's
+      // MFMAs. Only the barrier and the copies move with the role (uniform
+      // branches), so both roles share one register allocation. Each wave
+      // issues its share of the copies of interval j (K of j+1, V of j)
+      // inside interval j: the first role between its MFMA phase and softmax,
+      // the second after its softmax. Every wave runs n_int + 1 bodies, each
+      // with one barrier.
+      const bool second = PINGPONG && late;
+      auto body = [&](int jj, auto pv_flag, auto qk_flag, auto edge_flag) __attribute__((always_inline)) {
+        constexpr bool QK = decltype(qk_flag)::value;
+        mfma(jj, pv_flag, qk_flag);
+        __builtin_amdgcn_sched_barrier(0);
+        if (second) {
+          wait_copies();
+          __syncthreads();
+        } else {
+          copies(jj);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (QK) softmax_int(jj, edge_flag);
+        __builtin_amdgcn_sched_barrier(0);
+        if (second) {
+          copies(jj + 1);
+        } else {
+          wait_copies();
+          __syncthreads();
+        }
+      };
+      if (second) copies(0);
       if (n_live >= 1)
-        odd_interval(j++, F_{}, F_{}, F_{}, T_{});
+        body(j++, F_{}, T_{}, T_{});
       else
-        odd_interval(j++, F_{}, F_{}, F_{}, F_{});
-      for (; j < n_live; ++j) odd_interval(j, T_{}, F_{}, T_{}, T_{});   // steady state
-      if (j == n_live && j >= 1) odd_interval(j++, T_{}, T_{}, T_{}, F_{}); // last live pair
-      for (; j <= n_pairs; ++j) odd_interval(j, F_{}, F_{}, F_{}, F_{});  // idle
+        body(j++, F_{}, F_{}, F_{});
+      for (; j + 1 < n_live; ++j) body(j, T_{}, T_{}, F_{});  // steady state
+      if (j + 1 == n_live) body(j++, T_{}, T_{}, T_{});       // last live interval
+      if (j == n_live && j >= 1) body(j++, T_{}, F_{}, F_{}); // its P.V
+      for (; j <= n_int; ++j) body(j, F_{}, F_{}, F_{});      // idle: copies, barriers
     }
 
-    // Odd-tile waves hand their carriers to their even-tile partners.
-    float* xfer = reinterpret_cast<float*>(smem) + qgrp * 64 * G::CARRIER_FLOATS + lane;
-    if (parity == 1) {
+    // Carrier hand-off. Every wave leaves its carriers in LDS -- per pair of
+    // sub-tiles one 16-byte slot {m, d, m, d}, and the output blocks it does
+    // not finalise, one slot per block -- each lane at 16 * lane in a slot, so
+    // reads and writes are conflict-free. Then each wave merges the NPH
+    // carriers of its query group for its own blocks, db in
+    // [phase * OWN_DB, (phase + 1) * OWN_DB). Block and partner indices are
+    // compile-time (unrolled loops with wave-uniform branches on the phase),
+    // so no register array is indexed at run time. The last interval ended
+    // with a barrier, so the ring is no longer read.
+    f32x4* area = reinterpret_cast<f32x4*>(smem) + lane;
+    auto md_slot = [&](int w, int qs) { return area + (w * G::HANDOFF_SLOTS + qs / 2) * 64; };
+    auto o_slot = [&](int w, int qs, int db) {
+      return area + (w * G::HANDOFF_SLOTS + G::MD_SLOTS + qs * G::D_BLOCKS + db) * 64;
+    };
   #pragma unroll
-      for (int qs = 0; qs < QSUB; ++qs) {
-        float* x = xfer + qs * (2 + 4 * G::D_BLOCKS) * 64;
-        x[0] = cr[qs].m;
-        x[64] = cr[qs].d;
-  #pragma unroll
-        for (int db = 0; db < G::D_BLOCKS; ++db)
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) x[(2 + 4 * db + r) * 64] = cr[qs].o[db][r];
-      }
+    for (int qs = 0; qs < QSUB; qs += 2) {
+      f32x4 md;
+      md[0] = cr[qs].m;
+      md[1] = cr[qs].d;
+      md[2] = qs + 1 < QSUB ? cr[qs + 1].m : 0.0f;
+      md[3] = qs + 1 < QSUB ? cr[qs + 1].d : 0.0f;
+      *md_slot(wave, qs) = md;
     }
+  #pragma unroll
+    for (int qs = 0; qs < QSUB; ++qs)
+  #pragma unroll
+      for (int db = 0; db < G::D_BLOCKS; ++db)
+        if (db / G::OWN_DB != phase) *o_slot(wave, qs, db) = cr[qs].o[db];
     __syncthreads();
-    if (parity == 1) return;
 
     float* lse_h = lse + (int64_t)bh * S;
     _Float16* oh = o + head;
     const int64_t part_row0 = ((int64_t)split * BH + bh) * S;  // SPLIT: workspace rows
   #pragma unroll
     for (int qs = 0; qs < QSUB; ++qs) {
-      const float* x = xfer + qs * (2 + 4 * G::D_BLOCKS) * 64;
-      const float m2 = x[0];
-      const float m = __builtin_fmaxf(cr[qs].m, m2);
-      const float w1 = __builtin_amdgcn_exp2f(cr[qs].m - m);
-      const float w2 = __builtin_amdgcn_exp2f(m2 - m);
-      const float dsum = group_sum(cr[qs].d * w1 + x[64] * w2);
-      const int row = qrow0 + 16 * qs + li;
-      if constexpr (SPLIT) {
-        // A run can hold no visible key for a row (empty run, or causal keys
-        // above the row): its partial is o = 0 with weight 2^NEG_BIG = 0.
-        if (row < S) {
-          const bool empty = !(dsum > 0.0f);
-          const float inv = empty ? 0.0f : 1.0f / dsum;
-          float* po = part_o + (part_row0 + row) * D;
+      // merged max, each carrier's weight, and the row's denominator
+      float mp[NPH], dp[NPH], w[NPH];
+      float m = NEG_BIG;
   #pragma unroll
-          for (int db = 0; db < G::D_BLOCKS; ++db) {
-            f32x4 val;
-  #pragma unroll
-            for (int r = 0; r < 4; ++r) val[r] = (cr[qs].o[db][r] * w1 + x[(2 + 4 * db + r) * 64] * w2) * inv;
-            *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g) = val;
-          }
-          if (g == 0) part_lse[part_row0 + row] = empty ? NEG_BIG : m + log2f(dsum);
-        }
-        continue;
+      for (int p = 0; p < NPH; ++p) {
+        const f32x4 md = *md_slot(p * G::QGROUPS + qgrp, qs);
+        mp[p] = md[(qs & 1) * 2];
+        dp[p] = md[(qs & 1) * 2 + 1];
+        m = __builtin_fmaxf(m, mp[p]);
       }
-      const float inv = 1.0f / dsum;
+      float dl = 0.0f;
+  #pragma unroll
+      for (int p = 0; p < NPH; ++p) {
+        w[p] = __builtin_amdgcn_exp2f(mp[p] - m);
+        dl += dp[p] * w[p];
+      }
+      const float dsum = group_sum(dl);
+      const int row = qrow0 + 16 * qs + li;
+      // A run of a split can hold no visible key for a row (empty run, or
+      // causal keys above the row): its partial is o = 0 with weight
+      // 2^NEG_BIG = 0. A single pass always sees key 0.
+      const bool empty = SPLIT && !(dsum > 0.0f);
+      const float inv = empty ? 0.0f : 1.0f / dsum;
       if (row < S) {
   #pragma unroll
         for (int db = 0; db < G::D_BLOCKS; ++db) {
-          f16x4 h;
+          if (db / G::OWN_DB != phase) continue;
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            h[r] = (_Float16)((cr[qs].o[db][r] * w1 + x[(2 + 4 * db + r) * 64] * w2) * inv);
-          *reinterpret_cast<f16x4*>(oh + (int64_t)row * D + 16 * db + 4 * g) = h;
+          for (int p = 0; p < NPH; ++p) {
+            if (p == db / G::OWN_DB)
+              acc += cr[qs].o[db] * w[p];
+            else
+              acc += *o_slot(p * G::QGROUPS + qgrp, qs, db) * w[p];
+          }
+          if constexpr (SPLIT) {
+            float* po = part_o + (part_row0 + row) * D;
+            *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g) = acc * inv;
+          } else {
+            f16x4 h;
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) h[r] = (_Float16)(acc[r] * inv);
+            *reinterpret_cast<f16x4*>(oh + (int64_t)row * D + 16 * db + 4 * g) = h;
+          }
         }
-        if (g == 0) lse_h[row] = (m + log2f(dsum)) * 0.69314718055994530942f;
+        if (phase == 0 && g == 0) {
+          if constexpr (SPLIT)
+            part_lse[part_row0 + row] = empty ? NEG_BIG : m + log2f(dsum);
+          else
+            lse_h[row] = (m + log2f(dsum)) * 0.69314718055994530942f;
+        }
       }
     }
   };

@@ -114,6 +114,37 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      int B, int H, int S, int D, float scale, int causal, int n_splits,
                      void* workspace, size_t workspace_size, void* stream);
 
+/* Kernel variants for attn_fwd_variant (measured alternatives of the single
+ * pass; results agree with attn_fwd to rounding, not bitwise). */
+#define ATTN_VARIANT_DEFAULT 0   /* the kernel attn_fwd runs                    */
+#define ATTN_VARIANT_RING3 1     /* D = 64: three-slot K/V ring in LDS, copies   */
+                                 /* issued two key intervals ahead of their use  */
+#define ATTN_VARIANT_EXP_POLY 2  /* one exponential in four on the FMA path     */
+#define ATTN_VARIANT_WIDE 4      /* D = 64: 64-row waves over four 32-key tiles  */
+
+/*
+ * attn_fwd_variant -- attn_fwd with a chosen compiled variant of the kernel,
+ * for measurement and testing of the alternatives the pages discuss:
+ *  - ATTN_VARIANT_RING3: a deeper K/V ring ("Three kernels for a chip the
+ *    ecosystem skipped", Kernel one: a third buffer did not fit the 5090's
+ *    shared memory; "Learning FlashAttention the Hard Way, Part 2", Refused
+ *    Optimizations: deeper rings). Fits MI355X's 160 KB LDS at D = 64.
+ *  - ATTN_VARIANT_EXP_POLY: part of the exponentials computed by an FMA
+ *    polynomial instead of the transcendental unit (Part 2, Relationship to
+ *    FA-3 and FA-4: FlashAttention-4's emulated exponential).
+ *  - ATTN_VARIANT_WIDE: each wave owns 64 query rows instead of 32, halving
+ *    the LDS operand reads per MFMA (Part 2, Move 4: register tiling).
+ *
+ *  q ... causal, stream : as attn_fwd (same layouts, checks and status codes).
+ *  variant : one of the ATTN_VARIANT_* values; D = 64 builds 0, RING3,
+ *            EXP_POLY and WIDE, D = 128 builds 0 and EXP_POLY. Any other
+ *            value (or combination) returns ATTN_ERR_UNSUPPORTED before
+ *            anything is enqueued.
+ */
+int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int S, int D, float scale, int causal, int variant,
+                     void* stream);
+
 /* Workspace bytes attn_fwd_splitkv needs: n_splits * B * H * S * (D + 1) * 4
  * for n_splits > 1; 0 when n_splits == 1 or an argument is out of range. */
 size_t attn_fwd_splitkv_workspace_size(int B, int H, int S, int D, int n_splits);

@@ -189,3 +189,23 @@ def test_noalloc_invalid_arguments_are_rejected_on_host(name, kw, status):
                                        a["S"], a["D"], a["scale"], a["causal"], a["n_splits"], 0)
     assert _lib.STATUS_NAMES[rc] == status
     assert _lib.load().attn_last_error().decode()
+
+
+VARIANT_REFUSED = [
+    ("D128 ring3", dict(D=128, variant=1), "ATTN_ERR_UNSUPPORTED"),
+    ("D128 wide", dict(D=128, variant=4), "ATTN_ERR_UNSUPPORTED"),
+    ("combined flags", dict(variant=3), "ATTN_ERR_UNSUPPORTED"),
+    ("unknown flag", dict(variant=8), "ATTN_ERR_UNSUPPORTED"),
+    ("negative", dict(variant=-1), "ATTN_ERR_UNSUPPORTED"),
+    ("arguments checked first", dict(variant=99, q=0), "ATTN_ERR_NULL"),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", VARIANT_REFUSED, ids=[c[0] for c in VARIANT_REFUSED])
+def test_variant_refusals_on_host(name, kw, status):
+    a = dict(q=A, k=B_, v=C, o=O, lse=L, B=1, H=2, S=128, D=64, scale=0.125, causal=0, variant=0)
+    a.update(kw)
+    rc = _lib.attn_fwd_variant(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"],
+                               a["D"], a["scale"], a["causal"], a["variant"], 0)
+    assert _lib.STATUS_NAMES[rc] == status
+    assert _lib.load().attn_last_error().decode()

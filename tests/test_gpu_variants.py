@@ -1,0 +1,107 @@
+"""GPU parity of every compiled kernel variant (attn_fwd_variant) against the
+fp64 oracle, element by element over the whole output: the three-slot K/V
+ring and the 64-row waves at D = 64, and the exponential offload at both head
+dimensions. Shapes span several tiles with ragged tails, both masks, B > 1,
+negative and large scales, and rows whose running max moves mid-sequence."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import compare, gpu_available
+from testkit import WORKLOADS, make_qkv, workload_inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+# (D, variant) pairs built into the library, besides the default kernel
+BUILT = [(64, 1), (64, 2), (64, 4), (128, 2)]
+NAMES = {1: "ring3", 2: "exp_poly", 4: "wide"}
+
+SHAPES = [
+    # B, H, S, causal, scale, seed
+    (1, 2, 17, False, 0.125, 1),
+    (2, 3, 300, True, 0.125, 2),
+    (1, 2, 640, True, -0.2, 3),
+    (1, 1, 1000, False, 0.5, 4),
+    (3, 2, 385, False, None, 5),
+]
+
+
+def run_variant(q, k, v, scale, causal, variant):
+    import torch
+
+    import exact_attention_forward_05_amd as attn
+
+    dev = torch.device("cuda:0")
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (q, k, v))
+    o, lse = attn.fwd(qt, kt, vt, scale=scale, causal=causal, variant=variant)
+    torch.cuda.synchronize(dev)
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("D,variant", BUILT, ids=[f"D{d}-{NAMES[v]}" for d, v in BUILT])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda c: "B{}H{}S{}{}".format(
+    c[0], c[1], c[2], "c" if c[3] else "n"))
+def test_variant_small_shapes_full_compare(D, variant, shape):
+    B, H, S, causal, scale, seed = shape
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+    print(f"[gpu-variants] D{D} {NAMES[variant]} {shape}", flush=True)
+    q, k, v = make_qkv(B, H, S, D, 9500 + seed + D)
+    o, l = run_variant(q, k, v, scale, causal, variant)
+    O, L = oracle.sdpa_forward(q, k, v, scale, causal)
+    compare(o, l, O, L, f"D{D} {NAMES[variant]} {shape}")
+
+
+@pytest.mark.parametrize("D,variant", BUILT, ids=[f"D{d}-{NAMES[v]}" for d, v in BUILT])
+def test_variant_running_max_moves(D, variant):
+    """Peaked rows next to flat rows (Q x 4 / x 1/2 per 16-row half) and keys
+    scaled by 4 mid-sequence, both masks: the lazy max refreshes in some
+    sub-tiles only."""
+    for causal in (False, True):
+        q, k, v = make_qkv(1, 2, 700, D, 9600 + D + variant)
+        rows = np.arange(700)
+        q = q.astype(np.float32)
+        q[:, :, (rows % 32) < 16, :] *= 4.0
+        q[:, :, (rows % 32) >= 16, :] *= 0.5
+        k = k.astype(np.float32)
+        k[:, :, [200, 450, 601], :] *= 4.0
+        q, k = q.astype(np.float16), k.astype(np.float16)
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+        o, l = run_variant(q, k, v, scale, causal, variant)
+        O, L = oracle.sdpa_forward(q, k, v, scale, causal)
+        compare(o, l, O, L, f"lazy max D{D} {NAMES[variant]} causal={causal}")
+
+
+@pytest.mark.parametrize("variant", [1, 2, 4], ids=lambda v: NAMES[v])
+def test_variant_headline_full_compare(variant):
+    w = WORKLOADS["sdpa_b1h8s4096d64"]
+    q, k, v = workload_inputs(w)
+    o, l = run_variant(q, k, v, w.scale, w.causal, variant)
+    O, L = oracle.sdpa_forward(q, k, v, w.scale, w.causal)
+    print(f"[gpu-variants] headline {NAMES[variant]} "
+          f"{compare(o, l, O, L, f'headline {NAMES[variant]}')}", flush=True)
+
+
+def test_exp_poly_peaked_causal_d128():
+    """The exponential offload at D = 128 on a slice of the peaked causal
+    workload (Q, K x 3): 8 heads of S = 4096, every row compared."""
+    w = WORKLOADS["peaked_causal_b4h32s4096d128"]
+    q, k, v = (x[:1, :8] for x in workload_inputs(w))
+    q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+    o, l = run_variant(q, k, v, w.scale, True, 2)
+    O, L = oracle.sdpa_forward(q, k, v, w.scale, True)
+    print(f"[gpu-variants] peaked D128 exp_poly {compare(o, l, O, L, 'peaked exp_poly')}",
+          flush=True)
+
+
+def test_unbuilt_variant_is_refused():
+    import torch
+
+    import exact_attention_forward_05_amd as attn
+
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.float16, device="cuda:0")
+    with pytest.raises(attn.AttnError, match="ATTN_ERR_UNSUPPORTED"):
+        attn.fwd(q, q, q, variant=1)
