@@ -6,9 +6,12 @@ never calls it, imports nothing from it, and shares no code with it.
 
 What it computes (the plain definition, not the streaming method):
 
-  For fp16 Q, K, V of shape [B,H,S,D] and a softmax scale, for every batch b,
-  head h and query row i, with visible keys J_i = {0..S-1}, or {0..i} when
-  causal (key j > query i masked; the diagonal is visible):
+  For fp16 Q of shape [B,H,S_q,D], K and V of shape [B,H,S_k,D] and a softmax
+  scale, for every batch b, head h and query row i, with visible keys
+  J_i = {0..S_k-1}, or {0..i+S_k-S_q} when causal (the S_q queries are the
+  last S_q positions of the sequence; key j is masked when it lies after the
+  query's position; the diagonal is visible). With S_q = S_k = S this is
+  J_i = {0..i}:
 
     s_j   = scale * sum_d q_{i,d} k_{j,d}                  (j in J_i)
     m     = max_j s_j
@@ -23,9 +26,12 @@ Part 2: the workload definitions, and the unfused Move 0 kernels, which write
 the scores out, take the row max, the sum of exponentials, and then the
 normalised P times V). The error methodology is an fp64 reference over the
 identical fp16-rounded operands (the Emmy comments page, on hybrid FP16/FP32
-accumulation). Causal masking and the log-sum-exp output are not on the pages;
-the readings used are: causal hides key j from query i when j > i, and LSE is
-the natural log of sum_j exp(s_j) over the visible keys, with s already scaled.
+accumulation). Causal masking, the log-sum-exp output and queries against a
+longer key/value cache are not on the pages (the Emmy comments name decoding
+against a large KV cache); the readings used are: causal hides key j from
+query i when j > i + S_k - S_q (query i sits at position S_k - S_q + i, so
+with S_q = S_k it is j > i), and LSE is the natural log of sum_j exp(s_j) over
+the visible keys, with s already scaled.
 
 Inputs are promoted exactly from fp16 to fp64 and ``scale`` is the fp32 value
 the GPU receives, promoted to fp64. Outputs are fp64 and not rounded.
@@ -57,27 +63,34 @@ def _f64(x) -> np.ndarray:
     return a.astype(np.float64)
 
 
-def _check(q, k, v):
-    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError(f"Q, K, V must share one [B,H,S,D] shape: {q.shape} {k.shape} {v.shape}")
+def _check(q, k, v, causal: bool = False):
+    """Q [B,H,S_q,D], K and V [B,H,S_k,D]; causal needs S_q <= S_k (else the
+    first query rows would see no key)."""
+    if q.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"Q [B,H,S_q,D] and K, V [B,H,S_k,D] expected: {q.shape} {k.shape} {v.shape}")
+    if causal and q.shape[2] > k.shape[2]:
+        raise ValueError(f"causal attention needs S_q <= S_k: {q.shape[2]} > {k.shape[2]}")
 
 
-def _visible(rows: np.ndarray, S: int, causal: bool) -> np.ndarray:
-    """Boolean [len(rows), S]: key j visible to query row i."""
-    j = np.arange(S)
+def _visible(rows: np.ndarray, Sk: int, causal: bool, offset: int = 0) -> np.ndarray:
+    """Boolean [len(rows), S_k]: key j visible to query row i, i.e. every key,
+    or (causal) j <= i + offset with offset = S_k - S_q."""
+    j = np.arange(Sk)
     if not causal:
-        return np.ones((len(rows), S), dtype=bool)
-    return j[None, :] <= rows[:, None]
+        return np.ones((len(rows), Sk), dtype=bool)
+    return j[None, :] <= rows[:, None] + offset
 
 
 def _rows_of_head(qh, kh, vh, scale: float, causal: bool, rows: np.ndarray):
     """O and LSE (fp64) for the given query rows of one (b, h) head.
 
-    qh, kh, vh are fp64 [S, D]. Steps follow the definition in order.
+    qh is fp64 [S_q, D], kh and vh fp64 [S_k, D]. Steps follow the definition
+    in order.
     """
-    S = kh.shape[0]
-    s = scale * (qh[rows] @ kh.T)                      # scores [r, S]
-    s = np.where(_visible(rows, S, causal), s, -np.inf)
+    Sk = kh.shape[0]
+    offset = Sk - qh.shape[0]                          # query i sits at position offset + i
+    s = scale * (qh[rows] @ kh.T)                      # scores [r, S_k]
+    s = np.where(_visible(rows, Sk, causal, offset), s, -np.inf)
     m = s.max(axis=1, keepdims=True)                   # row max
     e = np.exp(s - m)                                  # masked keys -> 0
     d = e.sum(axis=1, keepdims=True)                   # denominator
@@ -88,8 +101,8 @@ def _rows_of_head(qh, kh, vh, scale: float, causal: bool, rows: np.ndarray):
 
 
 def sdpa_forward(q, k, v, scale: float, causal: bool = False):
-    """Full oracle: O fp64 [B,H,S,D] and LSE fp64 [B,H,S]."""
-    _check(q, k, v)
+    """Full oracle: O fp64 [B,H,S_q,D] and LSE fp64 [B,H,S_q]."""
+    _check(q, k, v, causal)
     B, H, S, D = q.shape
     scale = float(np.float32(scale))
     O = np.empty((B, H, S, D), dtype=np.float64)
@@ -105,7 +118,7 @@ def sdpa_forward(q, k, v, scale: float, causal: bool = False):
 
 def sdpa_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
     """Oracle O [len(rows), D] and LSE [len(rows)] for chosen rows of head (b, h)."""
-    _check(q, k, v)
+    _check(q, k, v, causal)
     rows = np.asarray(rows, dtype=np.int64)
     scale = float(np.float32(scale))
     return _rows_of_head(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), scale, causal, rows)
@@ -118,8 +131,9 @@ def partial_state(q, k, v, scale: float, causal: bool, key_lo: int, key_hi: int)
     d: [B,H,S] sum of exp(s - m), o: [B,H,S,D] sum of exp(s - m) v.
     A row with no visible key gets the identity (-inf, 0, 0).
     """
-    _check(q, k, v)
+    _check(q, k, v, causal)
     B, H, S, D = q.shape
+    Sk = k.shape[2]
     scale = float(np.float32(scale))
     m = np.full((B, H, S), -np.inf)
     d = np.zeros((B, H, S))
@@ -128,7 +142,7 @@ def partial_state(q, k, v, scale: float, causal: bool, key_lo: int, key_hi: int)
     if len(keys) == 0:
         return m, d, o
     rows = np.arange(S)
-    vis = _visible(rows, S, causal)[:, keys]
+    vis = _visible(rows, Sk, causal, Sk - S)[:, keys]
     for b in range(B):
         for h in range(H):
             qh, kh, vh = _f64(q[b, h]), _f64(k[b, h, keys]), _f64(v[b, h, keys])
@@ -174,17 +188,18 @@ def stream_fold(q, k, v, scale: float, causal: bool = False):
     after the deferred normalisation O = o / d. Loops over keys in Python, so
     it is meant for small S.
     """
-    _check(q, k, v)
+    _check(q, k, v, causal)
     B, H, S, D = q.shape
+    Sk = k.shape[2]
     scale = float(np.float32(scale))
     qf, kf, vf = _f64(q), _f64(k), _f64(v)
     m = np.full((B, H, S), -np.inf)
     d = np.zeros((B, H, S))
     o = np.zeros((B, H, S, D))
     rows = np.arange(S)
-    for j in range(S):
+    for j in range(Sk):
         s = scale * np.einsum("bhid,bhd->bhi", qf, kf[:, :, j, :])
-        vis = np.ones(S, dtype=bool) if not causal else (rows >= j)
+        vis = np.ones(S, dtype=bool) if not causal else (rows + (Sk - S) >= j)
         m_new = np.where(vis, np.maximum(m, s), m)
         with np.errstate(invalid="ignore"):
             alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)

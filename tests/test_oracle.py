@@ -211,9 +211,87 @@ def check_geometric_closed_form(sdpa):
             assert abs(L[0, 0, i] - lse) <= 1e-12
 
 
+# ---- queries against a longer key/value cache (S_q < S_k) ----------------
+
+def check_cache_bruteforce(sdpa):
+    """Pure-Python fp64 evaluation with S_q != S_k: query i sits at position
+    S_k - S_q + i, so under causal masking it sees keys 0 .. S_k - S_q + i."""
+    Sq, Sk, D = 3, 7, 4
+    q, _, _ = make_qkv(2, 2, Sq, D, 1601)
+    _, k, v = make_qkv(2, 2, Sk, D, 1602)
+    scale = 0.59375
+    for causal in (False, True):
+        O, L = sdpa(q, k, v, scale, causal)
+        assert O.shape == (2, 2, Sq, D) and L.shape == (2, 2, Sq)
+        qf, kf, vf = (x.astype(float).tolist() for x in (q, k, v))
+        for b in range(2):
+            for h in range(2):
+                for i in range(Sq):
+                    js = range(Sk - Sq + i + 1) if causal else range(Sk)
+                    w = {j: math.exp(scale * math.fsum(qf[b][h][i][d] * kf[b][h][j][d]
+                                                       for d in range(D))) for j in js}
+                    z = math.fsum(w.values())
+                    for d in range(D):
+                        ref = math.fsum(w[j] * vf[b][h][j][d] for j in js) / z
+                        assert abs(O[b, h, i, d] - ref) <= 1e-12, (b, h, i, d)
+                    assert abs(L[b, h, i] - math.log(z)) <= 1e-12
+
+
+def check_cache_suffix_of_square(sdpa):
+    """The last S_q rows of a square problem (S_k queries against the same K
+    and V) are exactly the queries-against-cache result for those S_q rows,
+    causal or not. This ties the S_q < S_k case to the square case."""
+    S, D = 29, 8
+    q, k, v = make_qkv(1, 2, S, D, 1603, qk_mult=2.0)
+    for causal in (False, True):
+        O, L = sdpa(q, k, v, 0.40625, causal)
+        for Sq in (1, 5, S):
+            O2, L2 = sdpa(np.ascontiguousarray(q[:, :, S - Sq:]), k, v, 0.40625, causal)
+            assert np.abs(O2 - O[:, :, S - Sq:]).max() <= 1e-12
+            assert np.abs(L2 - L[:, :, S - Sq:]).max() <= 1e-12
+
+
+def check_cache_torch_mask(sdpa):
+    """torch's scaled_dot_product_attention in float64 with the visibility as
+    an explicit boolean mask (True = visible), and torch.logsumexp of the
+    masked scores."""
+    Sq, Sk, D = 11, 40, 16
+    q, _, _ = make_qkv(2, 3, Sq, D, 1604)
+    _, k, v = make_qkv(2, 3, Sk, D, 1605)
+    for causal in (False, True):
+        vis = torch.ones(Sq, Sk, dtype=torch.bool)
+        if causal:
+            vis = torch.arange(Sk)[None, :] <= torch.arange(Sq)[:, None] + (Sk - Sq)
+        O, L = sdpa(q, k, v, 0.3125, causal)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            _t(q), _t(k), _t(v), attn_mask=vis, scale=0.3125)
+        assert np.abs(O - ref.numpy()).max() <= 1e-12
+        sc = 0.3125 * torch.matmul(_t(q), _t(k).transpose(-1, -2).contiguous())
+        sc = sc.masked_fill(~vis, -math.inf)
+        assert np.abs(L - torch.logsumexp(sc, dim=-1).numpy()).max() <= 1e-12
+
+
+def check_cache_equal_scores(sdpa):
+    """scale = 0 with S_q < S_k: O_i is the mean of the visible V rows
+    (v_0 .. v_{S_k-S_q+i} when causal, all S_k otherwise) and LSE_i = ln of
+    their count."""
+    Sq, Sk = 6, 19
+    q, _, _ = make_qkv(1, 2, Sq, 8, 1606)
+    _, k, v = make_qkv(1, 2, Sk, 8, 1607)
+    vf = v.astype(np.float64)
+    for causal in (False, True):
+        O, L = sdpa(q, k, v, 0.0, causal)
+        for i in range(Sq):
+            n = Sk - Sq + i + 1 if causal else Sk
+            assert np.abs(O[:, :, i] - vf[:, :, :n].mean(axis=2)).max() <= 1e-12
+            assert np.abs(L[:, :, i] - math.log(n)).max() <= 1e-12
+
+
 ALL_CHECKS = [check_bruteforce, check_torch_sdpa, check_rows_sum_to_one, check_constant_v,
               check_equal_scores, check_causal_row0, check_single_key, check_permutation,
-              check_bounds, check_last_row, check_one_hot, check_geometric_closed_form]
+              check_bounds, check_last_row, check_one_hot, check_geometric_closed_form,
+              check_cache_bruteforce, check_cache_suffix_of_square, check_cache_torch_mask,
+              check_cache_equal_scores]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -271,6 +349,33 @@ def test_sampled_rows_equal_full_oracle():
     assert np.abs(O2 - O[1, 2, rows]).max() <= 1e-13 and np.abs(L2 - L[1, 2, rows]).max() <= 1e-13
 
 
+def test_cache_partial_states_and_stream_fold():
+    """With S_q < S_k the carriers of split key ranges still merge to the
+    unsplit result, and the per-key streaming fold equals the definition."""
+    q, _, _ = make_qkv(2, 2, 9, 8, 1608, qk_mult=2.0)
+    _, k, v = make_qkv(2, 2, 30, 8, 1609)
+    for causal in (False, True):
+        O, L = oracle.sdpa_forward(q, k, v, 0.5, causal)
+        st = None
+        for a, b in ([0, 7], [7, 21], [21, 30]):
+            p = oracle.partial_state(q, k, v, 0.5, causal, a, b)
+            st = p if st is None else oracle.merge_states(st, p)
+        O2, L2 = oracle.finalize(st)
+        assert np.abs(O2 - O).max() <= 1e-12 and np.abs(L2 - L).max() <= 1e-12
+        O3, L3 = oracle.stream_fold(q, k, v, 0.5, causal)
+        assert np.abs(O3 - O).max() <= 1e-12 and np.abs(L3 - L).max() <= 1e-12
+
+
+def test_cache_shape_checks():
+    q, _, _ = make_qkv(1, 2, 9, 8, 1)
+    _, k, v = make_qkv(1, 2, 5, 8, 2)
+    oracle.sdpa_forward(q, k, v, 0.5, False)          # S_q > S_k is fine without a mask
+    with pytest.raises(ValueError):
+        oracle.sdpa_forward(q, k, v, 0.5, True)       # causal rows would see no key
+    with pytest.raises(ValueError):
+        oracle.sdpa_forward(q, k[:, :1], v[:, :1], 0.5, False)  # heads differ
+
+
 def test_oracle_rejects_non_fp16():
     q, k, v = make_qkv(1, 1, 4, 4, 1)
     with pytest.raises(TypeError):
@@ -303,6 +408,7 @@ def test_pages_workloads_and_flop_convention():
 def _mutant_rows(kind):
     def rows_of_head(qh, kh, vh, scale, causal, rows):
         S = kh.shape[0]
+        off = 0 if kind == "cache_top_left" else S - qh.shape[0]
         if kind == "transposed_qk":
             s = scale * (kh[rows] @ qh.T)
         elif kind == "no_scale":
@@ -312,7 +418,7 @@ def _mutant_rows(kind):
         else:
             s = scale * (qh[rows] @ kh.T)
         j = np.arange(S)[None, :]
-        i = rows[:, None]
+        i = rows[:, None] + off
         if causal:
             if kind == "mask_diagonal":
                 vis = j < i
@@ -337,7 +443,8 @@ def _mutant_rows(kind):
 
 
 MUTANTS = ["transposed_qk", "no_scale", "inverse_scale", "mask_diagonal", "mask_lower",
-           "exp2_base", "no_normalise", "reversed_v", "v_dims_swapped", "lse_no_max", "lse_log2"]
+           "exp2_base", "no_normalise", "reversed_v", "v_dims_swapped", "lse_no_max", "lse_log2",
+           "cache_top_left"]
 
 
 @pytest.mark.parametrize("kind", MUTANTS)
