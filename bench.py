@@ -48,8 +48,8 @@ def parse():
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the five-configuration timings, the sequence-length sweep "
-                         "(4k/8k/16k, B1 H8 D64), the split-KV comparison and the kernel "
-                         "variants")
+                         "(4k/8k/16k, B1 H8 D64), the split-KV comparison, the kernel "
+                         "variants and the key/value-cache (decode) timings")
     ap.add_argument("--sweep-steps", type=int, default=30,
                     help="timed launches per sweep point")
     ap.add_argument("--cold", action="store_true",
@@ -388,6 +388,55 @@ def run_variants(attn, dev, stream, steps, prewarm_ms):
     return out
 
 
+def run_decode(attn, dev, stream, steps, prewarm_ms):
+    """Queries against a key/value cache (attn_fwd_kvcache, split count from
+    the library's model): kernel time of the split pass plus the combine,
+    against the HBM roofline (K and V read once dominate the bytes)."""
+    import torch
+
+    from exact_attention_forward_05_amd import _lib
+    from testkit import DECODE, cache_inputs
+
+    out = []
+    for name, w in DECODE.items():
+        q, k, v = (torch.from_numpy(x).to(dev) for x in cache_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
+        ns = attn.choose_splits(w.B, w.H, w.Sq, w.D, w.causal,
+                                torch.cuda.get_device_properties(dev).multi_processor_count,
+                                Sk=w.Sk)
+        ws = torch.empty(max(16, attn.splitkv_workspace_size(w.B, w.H, w.Sq, w.D, ns)),
+                         dtype=torch.uint8, device=dev)
+        attn.fwd_kvcache(q, k, v, n_splits=ns, scale=w.scale, causal=w.causal, out=o, lse=lse,
+                         workspace=ws, stream=stream)
+        fn = getattr(_lib.load(), "attn_fwd_kvcache")
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
+                w.Sq, w.Sk, w.D, w.scale, int(w.causal), ns, ws.data_ptr(), ws.numel(),
+                stream.cuda_stream)
+
+        def step():
+            rc = fn(*args)
+            if rc:
+                _lib.check(rc)
+        prewarm(step, prewarm_ms)
+        for _ in range(5):
+            step()
+        durs, _ = time_launches(step, stream, steps)
+        us = float(durs.mean()) * 1e3
+        # partial results written and read back by the combine (fp32 o/d and lse)
+        part = 2 * ns * w.B * w.H * w.Sq * (w.D + 1) * 4 if ns > 1 else 0
+        rec = {"workload": name, "B": w.B, "H": w.H, "S_q": w.Sq, "S_k": w.Sk, "D": w.D,
+               "causal": w.causal, "n_splits": ns, "us_mean": round(us, 3),
+               "algorithmic_bytes": w.algorithmic_bytes, "partial_bytes": part,
+               "hbm_gbs": round(w.algorithmic_bytes / (us * 1e-6) / 1e9, 1),
+               "hbm_frac": round(w.algorithmic_bytes / (us * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
+               "tflops": round(w.flops / (us * 1e-6) / 1e12, 2)}
+        log(f"decode {rec}")
+        out.append(rec)
+        del q, k, v, o, lse, ws
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -500,6 +549,7 @@ def main():
         result["sweep"] = run_sweep(attn, dev, stream, args.sweep_steps, point_ms)
         result["splitkv"] = run_splitkv(attn, dev, stream, args.sweep_steps, point_ms)
         result["variants"] = run_variants(attn, dev, stream, args.sweep_steps, point_ms)
+        result["decode"] = run_decode(attn, dev, stream, args.sweep_steps, point_ms)
     if not args.no_cpu_baseline:
         log("CPU oracle leg ...")
         o_np = o.cpu().numpy()

@@ -26,6 +26,10 @@ _SIGNATURES = [
      [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
       ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("attn_fwd_kvcache", ctypes.c_int,
+     [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+      ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     ("attn_fwd_variant", ctypes.c_int,
      [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
@@ -77,6 +81,15 @@ def attn_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: in
     """Raw call of the C entry point with integer addresses; returns the status."""
     return load().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D,
                            ctypes.c_float(scale), causal, stream)
+
+
+def attn_fwd_kvcache(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
+                     S_q: int, S_k: int, D: int, scale: float, causal: int, n_splits: int,
+                     ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    """Raw call of the key/value-cache entry point; returns the status."""
+    return load().attn_fwd_kvcache(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D,
+                                   ctypes.c_float(scale), causal, n_splits, ws_ptr, ws_bytes,
+                                   stream)
 
 
 # Kernel variants (ATTN_VARIANT_*) and the head dimensions each is built for.

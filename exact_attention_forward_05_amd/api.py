@@ -92,19 +92,33 @@ _INTERVAL_US = {64: 1.05, 128: 1.6}
 _TILE_FIXED = 1.0
 _COMBINE_GBS = 4000.0
 _COMBINE_FIXED_US = 3.0
-_SPLIT_CHOICES = (1, 2, 3, 4, 6, 8, 12, 16)
+_SPLIT_CHOICES = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64)
+
+
+def _intervals_per_tile(Sq: int, Sk: int, causal: bool) -> list:
+    """Key intervals (of PAIR_KEYS keys) each query tile folds: all of S_k, or
+    (causal; queries at positions S_k - S_q + i) the keys up to the tile's
+    last query."""
+    n_qt = -(-Sq // BLOCK_M)
+    n_all = -(-Sk // PAIR_KEYS)
+    if not causal:
+        return [n_all] * n_qt
+    off = Sk - Sq
+    return [-(-min(Sk, BLOCK_M * (t + 1) + off) // PAIR_KEYS) for t in range(n_qt)]
 
 
 @functools.lru_cache(maxsize=256)
-def _workgroup_costs(B: int, H: int, S: int, causal: bool, s: int, n_cus: int) -> list:
+def _workgroup_costs(B: int, H: int, S: int, causal: bool, s: int, n_cus: int,
+                     Sk: Optional[int] = None) -> list:
     """Cost of every workgroup of a launch with ``s`` runs (one pass when
-    s == 1), in key-tile-pair intervals plus a fixed cost per query tile that
-    a workgroup loads, following the kernel's work orders: each query tile's
-    pairs are cut into ``s`` runs; a causal single pass folds mirror pairs of
-    tiles (n_qtiles + 1 pairs, two tiles loaded) when that still fills the
-    CUs."""
+    s == 1), in key intervals plus a fixed cost per query tile that a
+    workgroup loads, following the kernel's work orders: each query tile's
+    intervals are cut into ``s`` runs; a causal single pass folds mirror
+    pairs of tiles (two tiles loaded) when that still fills the CUs. ``S`` is
+    the query length, ``Sk`` the key length (default ``S``)."""
+    Sk = S if Sk is None else Sk
     n_qt = -(-S // BLOCK_M)
-    pairs = [i + 1 if causal else n_qt for i in range(n_qt)]
+    pairs = _intervals_per_tile(S, Sk, causal)
     costs = []
     if s == 1 and causal and B * H * ((n_qt + 1) // 2) >= n_cus:
         for u in range((n_qt + 1) // 2):
@@ -118,7 +132,8 @@ def _workgroup_costs(B: int, H: int, S: int, causal: bool, s: int, n_cus: int) -
     return costs * (B * H)
 
 
-def choose_splits(B: int, H: int, S: int, D: int, causal: bool, n_cus: int = 256) -> int:
+def choose_splits(B: int, H: int, S: int, D: int, causal: bool, n_cus: int = 256,
+                  Sk: Optional[int] = None) -> int:
     """Split count for attn_fwd_splitkv from a small cost model.
 
     Each workgroup (one per CU: at D = 64 the registers of its eight waves,
@@ -132,11 +147,12 @@ def choose_splits(B: int, H: int, S: int, D: int, causal: bool, n_cus: int = 256
     n_qt = -(-S // BLOCK_M)
     if B * H * n_qt >= 4 * n_cus and not causal:
         return 1
+    longest = max(_intervals_per_tile(S, S if Sk is None else Sk, causal))
     best, best_us = 1, math.inf
     for s in _SPLIT_CHOICES:
-        if s > max(1, n_qt):  # never more runs than the longest tile has pairs
+        if s > max(1, longest):  # never more runs than the longest tile has intervals
             break
-        costs = sorted(_workgroup_costs(B, H, S, causal, s, n_cus), reverse=True)
+        costs = sorted(_workgroup_costs(B, H, S, causal, s, n_cus, Sk), reverse=True)
         if len(costs) > 200000:
             break
         loads = [0.0] * min(n_cus, len(costs))
@@ -181,5 +197,65 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         st = _lib.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    lse.data_ptr(), B, H, S, D, scale, int(bool(causal)),
                                    n_splits, ws_ptr, ws_bytes, stream.cuda_stream)
+    _lib.check(st)
+    return out, lse
+
+
+def fwd_kvcache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                n_splits: Union[int, str] = "auto", scale: Optional[float] = None,
+                causal: bool = False, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Queries against a key/value cache: q [B, H, S_q, D], k and v
+    [B, H, S_k, D] (fp16, contiguous, one device). The queries are the last
+    S_q positions, so ``causal`` hides from query i the keys after position
+    S_k - S_q + i (needs S_q <= S_k). Returns (o [B, H, S_q, D] fp16, lse
+    [B, H, S_q] fp32). Split-KV over the keys (``n_splits``, "auto" =
+    :func:`choose_splits`), with an optional uint8 ``workspace``.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA tensor")
+        if t.dtype != torch.float16 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D float16 tensor")
+    if k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"q [B,H,S_q,D] and k, v [B,H,S_k,D] expected: "
+                         f"{tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must be on one device")
+    B, H, Sq, D = (int(x) for x in q.shape)
+    Sk = int(k.shape[2])
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous fp16 tensor shaped like q on q's device")
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 tensor [B,H,S_q] on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    if n_splits == "auto":
+        n_splits = choose_splits(B, H, Sq, D, bool(causal),
+                                 torch.cuda.get_device_properties(q.device).multi_processor_count,
+                                 Sk=Sk)
+    n_splits = int(n_splits)
+    need = _lib.splitkv_workspace_size(B, H, Sq, D, n_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous CUDA tensor on q's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = _lib.attn_fwd_kvcache(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, H, Sq, Sk, D, float(scale),
+                                   int(bool(causal)), n_splits, ws_ptr, ws_bytes,
+                                   stream.cuda_stream)
     _lib.check(st)
     return out, lse

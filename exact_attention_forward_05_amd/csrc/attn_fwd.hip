@@ -24,12 +24,13 @@ thread_local char g_last_error[512] = "";
 
 attn::plan::Msg msg() { return attn::plan::Msg{g_last_error, sizeof(g_last_error)}; }
 
+// Sq query rows against Sk keys per head (Sq == Sk for self-attention).
 template <int D, bool CAUSAL, int VAR = 0>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-           int S, float scale, int n_splits, void* workspace, hipStream_t stream) {
+           int Sq, int Sk, float scale, int n_splits, void* workspace, hipStream_t stream) {
   using namespace attn;
   plan::Launch L;
-  const int rc = plan::make_launch(B, H, S, D, CAUSAL ? 1 : 0, n_splits, &L, msg());
+  const int rc = plan::make_launch(B, H, Sq, D, CAUSAL ? 1 : 0, n_splits, &L, msg());
   if (rc != ATTN_OK) return rc;
   const int BH = B * H;
   // Scores are folded in base 2: t = s * |scale| * log2(e). A negative scale
@@ -42,19 +43,19 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   _Float16* oh = static_cast<_Float16*>(o);
   if (n_splits == 1) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, VAR>), dim3((unsigned)L.blocks),
-                       dim3(THREADS), 0, stream, qh, kh, vh, oh, lse, BH, S, L.n_qtiles, 1,
+                       dim3(THREADS), 0, stream, qh, kh, vh, oh, lse, BH, Sq, Sk, L.n_qtiles, 1,
                        L.order, c, qsign, nullptr, nullptr);
   } else if constexpr (VAR == 0) {
     float* part_o = static_cast<float*>(workspace);
     float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                               plan::part_o_bytes(B, H, S, D, n_splits));
+                                               plan::part_o_bytes(B, H, Sq, D, n_splits));
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, true>), dim3((unsigned)L.blocks),
-                       dim3(THREADS), 0, stream, qh, kh, vh, oh, lse, BH, S, L.n_qtiles,
+                       dim3(THREADS), 0, stream, qh, kh, vh, oh, lse, BH, Sq, Sk, L.n_qtiles,
                        n_splits, L.order, c, qsign, part_o, part_lse);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
       return plan::fail(msg(), ATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
-    const int64_t rows = (int64_t)BH * S;
+    const int64_t rows = (int64_t)BH * Sq;
     hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)L.combine_blocks),
                        dim3(plan::COMBINE_THREADS), 0, stream, part_o, part_lse, oh, lse, rows,
                        n_splits);
@@ -66,14 +67,14 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
 }
 
 int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-             int S, int D, float scale, int causal, int n_splits, void* workspace,
+             int Sq, int Sk, int D, float scale, int causal, int n_splits, void* workspace,
              void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (D == 64)
-    return causal ? launch<64, true>(q, k, v, o, lse, B, H, S, scale, n_splits, workspace, st)
-                  : launch<64, false>(q, k, v, o, lse, B, H, S, scale, n_splits, workspace, st);
-  return causal ? launch<128, true>(q, k, v, o, lse, B, H, S, scale, n_splits, workspace, st)
-                : launch<128, false>(q, k, v, o, lse, B, H, S, scale, n_splits, workspace, st);
+    return causal ? launch<64, true>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_splits, workspace, st)
+                  : launch<64, false>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_splits, workspace, st);
+  return causal ? launch<128, true>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_splits, workspace, st)
+                : launch<128, false>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_splits, workspace, st);
 }
 
 // Single pass of a compiled kernel variant (attn::VAR_* flags), or
@@ -81,8 +82,8 @@ int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, i
 template <int D, int VAR>
 int launch_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int H, int S, float scale, int causal, hipStream_t st) {
-  return causal ? launch<D, true, VAR>(q, k, v, o, lse, B, H, S, scale, 1, nullptr, st)
-                : launch<D, false, VAR>(q, k, v, o, lse, B, H, S, scale, 1, nullptr, st);
+  return causal ? launch<D, true, VAR>(q, k, v, o, lse, B, H, S, S, scale, 1, nullptr, st)
+                : launch<D, false, VAR>(q, k, v, o, lse, B, H, S, S, scale, 1, nullptr, st);
 }
 
 int dispatch_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -110,17 +111,34 @@ int dispatch_variant(const void* q, const void* k, const void* v, void* o, float
                           ATTN_VARIANT_WIDE, ATTN_VARIANT_EXP_POLY);
 }
 
+// Checks shared by the entry points (Sq query rows against Sk keys).
 int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                 int B, int H, int S, int D, float scale, int causal, int n_splits) {
-  const int rc = attn::plan::check_args(q, k, v, o, lse, B, H, S, S, D, scale, causal, msg());
+                 int B, int H, int Sq, int Sk, int D, float scale, int causal, int n_splits) {
+  const int rc = attn::plan::check_args(q, k, v, o, lse, B, H, Sq, Sk, D, scale, causal, msg());
   if (rc != ATTN_OK) return rc;
   if (n_splits < 1 || n_splits > ATTN_MAX_SPLITS)
     return attn::plan::fail(msg(), ATTN_ERR_ARG, "n_splits must be in [1, %d] (got %d)",
                             ATTN_MAX_SPLITS, n_splits);
-  if (n_splits > 1 && attn::plan::workspace_size(B, H, S, D, n_splits) == 0)
+  if (n_splits > 1 && attn::plan::workspace_size(B, H, Sq, D, n_splits) == 0)
     return attn::plan::fail(msg(), ATTN_ERR_SHAPE, "workspace size overflows");
   attn::plan::Launch L;  // grid limits, checked before anything is enqueued
-  return attn::plan::make_launch(B, H, S, D, causal, n_splits, &L, msg());
+  return attn::plan::make_launch(B, H, Sq, D, causal, n_splits, &L, msg());
+}
+
+// The workspace checks of the split entry points (n_splits > 1).
+int check_workspace(const void* workspace, size_t workspace_size, int B, int H, int Sq, int D,
+                    int n_splits) {
+  if (n_splits == 1) return ATTN_OK;
+  if (!workspace)
+    return attn::plan::fail(msg(), ATTN_ERR_NULL, "workspace is NULL with n_splits=%d", n_splits);
+  if (!attn::plan::aligned(workspace, 16))
+    return attn::plan::fail(msg(), ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const size_t need = attn::plan::workspace_size(B, H, Sq, D, n_splits);
+  if (workspace_size < need)
+    return attn::plan::fail(msg(), ATTN_ERR_ARG,
+                            "workspace of %zu bytes is smaller than the %zu bytes needed",
+                            workspace_size, need);
+  return ATTN_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -165,15 +183,15 @@ extern "C" {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int S, int D, float scale, int causal, void* stream) {
   g_last_error[0] = '\0';
-  const int rc = check_common(q, k, v, o, lse, B, H, S, D, scale, causal, 1);
+  const int rc = check_common(q, k, v, o, lse, B, H, S, S, D, scale, causal, 1);
   if (rc != ATTN_OK) return rc;
-  return dispatch(q, k, v, o, lse, B, H, S, D, scale, causal, 1, nullptr, stream);
+  return dispatch(q, k, v, o, lse, B, H, S, S, D, scale, causal, 1, nullptr, stream);
 }
 
 int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int H, int S, int D, float scale, int causal, int variant, void* stream) {
   g_last_error[0] = '\0';
-  const int rc = check_common(q, k, v, o, lse, B, H, S, D, scale, causal, 1);
+  const int rc = check_common(q, k, v, o, lse, B, H, S, S, D, scale, causal, 1);
   if (rc != ATTN_OK) return rc;
   return dispatch_variant(q, k, v, o, lse, B, H, S, D, scale, causal, variant, stream);
 }
@@ -186,28 +204,29 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      int H, int S, int D, float scale, int causal, int n_splits,
                      void* workspace, size_t workspace_size, void* stream) {
   g_last_error[0] = '\0';
-  const int rc = check_common(q, k, v, o, lse, B, H, S, D, scale, causal, n_splits);
+  int rc = check_common(q, k, v, o, lse, B, H, S, S, D, scale, causal, n_splits);
   if (rc != ATTN_OK) return rc;
-  if (n_splits > 1) {
-    if (!workspace)
-      return attn::plan::fail(msg(), ATTN_ERR_NULL, "workspace is NULL with n_splits=%d",
-                              n_splits);
-    if (!attn::plan::aligned(workspace, 16))
-      return attn::plan::fail(msg(), ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
-    const size_t need = attn::plan::workspace_size(B, H, S, D, n_splits);
-    if (workspace_size < need)
-      return attn::plan::fail(msg(), ATTN_ERR_ARG,
-                              "workspace of %zu bytes is smaller than the %zu bytes needed",
-                              workspace_size, need);
-  }
-  return dispatch(q, k, v, o, lse, B, H, S, D, scale, causal, n_splits, workspace, stream);
+  rc = check_workspace(workspace, workspace_size, B, H, S, D, n_splits);
+  if (rc != ATTN_OK) return rc;
+  return dispatch(q, k, v, o, lse, B, H, S, S, D, scale, causal, n_splits, workspace, stream);
+}
+
+int attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int S_q, int S_k, int D, float scale, int causal, int n_splits,
+                     void* workspace, size_t workspace_size, void* stream) {
+  g_last_error[0] = '\0';
+  int rc = check_common(q, k, v, o, lse, B, H, S_q, S_k, D, scale, causal, n_splits);
+  if (rc != ATTN_OK) return rc;
+  rc = check_workspace(workspace, workspace_size, B, H, S_q, D, n_splits);
+  if (rc != ATTN_OK) return rc;
+  return dispatch(q, k, v, o, lse, B, H, S_q, S_k, D, scale, causal, n_splits, workspace, stream);
 }
 
 int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
                              int B, int H, int S, int D, float scale, int causal, int n_splits,
                              void* stream) {
   g_last_error[0] = '\0';
-  const int rc = check_common(q, k, v, o, lse, B, H, S, D, scale, causal, n_splits);
+  const int rc = check_common(q, k, v, o, lse, B, H, S, S, D, scale, causal, n_splits);
   if (rc != ATTN_OK) return rc;
   void* ws = nullptr;
   if (n_splits > 1) {
@@ -223,7 +242,7 @@ int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* 
   }
   // Every partial result the combine kernel reads is written by the split
   // kernel of the same call first, so the scratch needs no clearing.
-  return dispatch(q, k, v, o, lse, B, H, S, D, scale, causal, n_splits, ws, stream);
+  return dispatch(q, k, v, o, lse, B, H, S, S, D, scale, causal, n_splits, ws, stream);
 }
 
 const char* attn_status_string(int status) {

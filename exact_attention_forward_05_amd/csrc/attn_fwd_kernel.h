@@ -469,10 +469,12 @@ template <int D, int VAR, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
                                              const ScoreSet<D, VAR>& sc,
                                              ProbSet<D, VAR>& pf, float c, int key0,
-                                             int qrow0, int S, int li, int g) {
+                                             int qpos0, int S, int li, int g) {
   using G = Geometry<D, VAR>;
   constexpr int QSUB = G::QSUB;
-  // hidden-key bits per sub-tile and key block (bit r: accumulator element r)
+  // hidden-key bits per sub-tile and key block (bit r: accumulator element
+  // r): keys past S, and (causal) keys after the query's sequence position
+  // (qpos0 is the position of the wave's first row)
   uint32_t hid[QSUB][G::KB];
 #pragma unroll
   for (int qs = 0; qs < QSUB; ++qs)
@@ -480,11 +482,11 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
     for (int kb = 0; kb < G::KB; ++kb) {
       hid[qs][kb] = 0u;
       if (MASK) {
-        const int qrow = qrow0 + 16 * qs + li;
+        const int qpos = qpos0 + 16 * qs + li;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = key0 + 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
-          const bool h = key >= S || (CAUSAL && key > qrow);
+          const bool h = key >= S || (CAUSAL && key > qpos);
           hid[qs][kb] |= (h ? 1u : 0u) << r;
         }
       }
@@ -567,15 +569,15 @@ template <int D, int VAR, bool CAUSAL>
 __device__ __forceinline__ void softmax_any(CarrierSet<D, VAR>& cr,
                                             const ScoreSet<D, VAR>& sc,
                                             ProbSet<D, VAR>& pf, float c, int key0,
-                                            int qrow0, int S, int li, int g) {
+                                            int qpos0, int S, int li, int g) {
   constexpr int BN = Geometry<D, VAR>::BN;
   // Element masks are needed on the sequence tail and on tiles reaching past
-  // the wave's first query (causal diagonal).
-  const bool needs_mask = (key0 + BN > S) || (CAUSAL && key0 + BN - 1 > qrow0);
+  // the position of the wave's first query (causal diagonal).
+  const bool needs_mask = (key0 + BN > S) || (CAUSAL && key0 + BN - 1 > qpos0);
   if (needs_mask)
-    softmax_tile<D, VAR, CAUSAL, true>(cr, sc, pf, c, key0, qrow0, S, li, g);
+    softmax_tile<D, VAR, CAUSAL, true>(cr, sc, pf, c, key0, qpos0, S, li, g);
   else
-    softmax_tile<D, VAR, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
+    softmax_tile<D, VAR, CAUSAL, false>(cr, sc, pf, c, key0, qpos0, S, li, g);
 }
 
 // Workgroup id -> (batch*head, query tiles) by `order` (work_order.h).
@@ -598,7 +600,7 @@ template <int D, bool CAUSAL, bool SPLIT, int VAR = 0>
 __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
-    int BH, int S, int n_qtiles, int n_splits, int order, float c, uint32_t qsign,
+    int BH, int Sq, int Sk, int n_qtiles, int n_splits, int order, float c, uint32_t qsign,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
   using G = Geometry<D, VAR>;
   constexpr int R = G::RING;
@@ -613,10 +615,15 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
   const int bid = SPLIT ? (int)(blockIdx.x / (unsigned)n_splits) : (int)blockIdx.x;
   const TileWork work = work_of(SPLIT ? ORDER_TILES : order, bid, BH, n_qtiles);
   const int bh = work.bh;
-  const int64_t head = (int64_t)bh * S * D;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, (uint32_t)S * D * 2);
-  const _Float16* kh = k + head;
-  const _Float16* vh = v + head;
+  const int64_t qhead = (int64_t)bh * Sq * D;   // Q and O of this head
+  const int64_t kvhead = (int64_t)bh * Sk * D;  // K and V of this head
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + qhead, (uint32_t)Sq * D * 2);
+  const _Float16* kh = k + kvhead;
+  const _Float16* vh = v + kvhead;
+  // Query row i sits at sequence position i + koff (the queries are the last
+  // Sq positions); causal masking hides keys after a query's position.
+  const int koff = Sk - Sq;
+  const int S = Sk;  // keys per head: the range of the K/V descriptors and masks
 
   // One query tile: Q load, the key loop and the epilogue.
   auto run_tile = [&](const int qt) __attribute__((always_inline)) {
@@ -634,6 +641,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const bool late = wave >= WAVES / 2;  // second wave of its SIMD
     const int q0 = qt * BLOCK_M;
     const int qrow0 = q0 + G::ROWS * qgrp;  // this wave's first query row
+    const int qpos0 = qrow0 + koff;         // its sequence position
 
     // Q^T fragments, loaded once (sign-flipped when the scale is negative):
     // into registers, or (Q_IN_LDS) the workgroup's Q rows into LDS by direct
@@ -683,7 +691,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     f16x8 pf[QSUB][G::KC];
     f32x4 sc[QSUB][G::KB];
 
-    const int kend = CAUSAL ? min(S, q0 + BLOCK_M) : S;
+    const int kend = CAUSAL ? min(S, q0 + BLOCK_M + koff) : S;
     const int n_kt = (kend + G::BN - 1) / G::BN;
     const int n_int_all = (n_kt + NPH - 1) / NPH;
     // This workgroup folds intervals [pb, pb + n_int): all of them, or its
@@ -692,10 +700,11 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const int n_int = SPLIT ? (int)((int64_t)(split + 1) * n_int_all / n_splits) - pb : n_int_all;
     // Intervals whose tile of this wave's phase holds keys for its rows: a
     // prefix, since tiles past S or past the wave's last query (causal) are
-    // skipped.
-    const int row_end = CAUSAL ? min(kend, qrow0 + G::ROWS) : kend;  // keys < row_end are needed
+    // skipped. A wave with no query row below Sq (the last query tile of a
+    // short query block) only copies and synchronises.
+    const int row_end = CAUSAL ? min(kend, qpos0 + G::ROWS) : kend;  // keys < row_end are needed
     const int live_tiles = (row_end + G::BN - 1) / G::BN;
-    const int n_live = min(max((live_tiles - phase + NPH - 1) / NPH - pb, 0), n_int);
+    const int n_live = qrow0 >= Sq ? 0 : min(max((live_tiles - phase + NPH - 1) / NPH - pb, 0), n_int);
     constexpr bool PINGPONG = G::PINGPONG;
     // Only the last live interval of a wave can need element masks: the
     // sequence tail is in the last tile, and the tiles crossing the causal
@@ -746,9 +755,9 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(2);
       const int key0 = (pb + p) * INTERVAL_KEYS + phase * G::BN;
       if constexpr (decltype(edge_flag)::value)
-        softmax_any<D, VAR, CAUSAL>(cr, sc, pf, c, key0, qrow0, S, li, g);
+        softmax_any<D, VAR, CAUSAL>(cr, sc, pf, c, key0, qpos0, S, li, g);
       else
-        softmax_tile<D, VAR, CAUSAL, false>(cr, sc, pf, c, key0, qrow0, S, li, g);
+        softmax_tile<D, VAR, CAUSAL, false>(cr, sc, pf, c, key0, qpos0, S, li, g);
       if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(0);
     };
     auto mfma = [&](int j, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
@@ -911,9 +920,9 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
         if (db / G::OWN_DB != phase) *o_slot(wave, qs, db) = cr[qs].o[db];
     __syncthreads();
 
-    float* lse_h = lse + (int64_t)bh * S;
-    _Float16* oh = o + head;
-    const int64_t part_row0 = ((int64_t)split * BH + bh) * S;  // SPLIT: workspace rows
+    float* lse_h = lse + (int64_t)bh * Sq;
+    _Float16* oh = o + qhead;
+    const int64_t part_row0 = ((int64_t)split * BH + bh) * Sq;  // SPLIT: workspace rows
   #pragma unroll
     for (int qs = 0; qs < QSUB; ++qs) {
       // merged max, each carrier's weight, and the row's denominator
@@ -939,7 +948,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       // 2^NEG_BIG = 0. A single pass always sees key 0.
       const bool empty = SPLIT && !(dsum > 0.0f);
       const float inv = empty ? 0.0f : 1.0f / dsum;
-      if (row < S) {
+      if (row < Sq) {
   #pragma unroll
         for (int db = 0; db < G::D_BLOCKS; ++db) {
           if (db / G::OWN_DB != phase) continue;

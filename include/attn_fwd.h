@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 2
+#define ATTN_FWD_ABI_VERSION 3
 
 /* Largest n_splits accepted by attn_fwd_splitkv. */
 #define ATTN_MAX_SPLITS 64
@@ -145,8 +145,33 @@ int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float
                      int B, int H, int S, int D, float scale, int causal, int variant,
                      void* stream);
 
+/*
+ * attn_fwd_kvcache -- S_q queries per head against S_k cached keys and values
+ * (decoding, or a chunk of new tokens, against a key/value cache; the Emmy
+ * comments page closes on split-KV as what matters when decoding against a
+ * large KV cache, and Part 2's references name Flash-Decoding). The queries
+ * are the last S_q positions of the sequence: with causal = 1, query row i
+ * (position S_k - S_q + i) sees keys 0 .. S_k - S_q + i; with S_q = S_k this
+ * is attn_fwd_splitkv exactly.
+ *
+ *  q    : fp16 [B, H, S_q, D], contiguous; o : fp16 [B, H, S_q, D];
+ *  lse  : fp32 [B, H, S_q];
+ *  k, v : fp16 [B, H, S_k, D], contiguous (the cache, read only);
+ *  S_q, S_k : >= 1; causal = 1 needs S_q <= S_k (else ATTN_ERR_SHAPE);
+ *  n_splits, workspace, workspace_size : as attn_fwd_splitkv, with the
+ *             workspace sized by attn_fwd_splitkv_workspace_size(B, H, S_q,
+ *             D, n_splits) (partials are per query row). Few query rows make
+ *             few workgroups, so decoding wants n_splits > 1 (each run of
+ *             keys gets its own workgroups).
+ *  Other arguments, alignment, ownership and status codes: as attn_fwd.
+ */
+int attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int S_q, int S_k, int D, float scale, int causal,
+                     int n_splits, void* workspace, size_t workspace_size, void* stream);
+
 /* Workspace bytes attn_fwd_splitkv needs: n_splits * B * H * S * (D + 1) * 4
- * for n_splits > 1; 0 when n_splits == 1 or an argument is out of range. */
+ * for n_splits > 1; 0 when n_splits == 1 or an argument is out of range.
+ * For attn_fwd_kvcache pass S = S_q. */
 size_t attn_fwd_splitkv_workspace_size(int B, int H, int S, int D, int n_splits);
 
 /* Size of the static device scratch buffer of attn_fwd_splitkv_noalloc. */

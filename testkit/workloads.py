@@ -114,3 +114,60 @@ def make_qkv(B: int, H: int, S: int, D: int, seed: int,
 
 def workload_inputs(w: Workload):
     return make_qkv(w.B, w.H, w.S, w.D, w.seed, w.qk_mult, w.v_mult)
+
+
+@dataclass(frozen=True)
+class CacheWorkload:
+    """S_q queries per head against an S_k-key cache (the queries are the
+    last S_q positions). Q uses stream 0 of ``seed``, K and V streams 1 and 2
+    of ``seed + 1``."""
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.D)))
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """K and V read once, Q read and O written once (fp16), LSE (fp32)."""
+        bh = self.B * self.H
+        return 2 * bh * self.Sk * self.D * 2 + 2 * bh * self.Sq * self.D * 2 + bh * self.Sq * 4
+
+    @property
+    def flops(self) -> float:
+        """4 * D per visible (query, key) pair."""
+        off = self.Sk - self.Sq
+        if self.causal:
+            vis = sum(min(self.Sk, off + i + 1) for i in range(self.Sq))
+        else:
+            vis = self.Sq * self.Sk
+        return 4.0 * self.B * self.H * self.D * vis
+
+    def describe(self) -> str:
+        m = "causal" if self.causal else "non-causal"
+        return f"B{self.B} H{self.H} S_q{self.Sq} S_k{self.Sk} D{self.D} fp16 {m}"
+
+
+def cache_inputs(w: CacheWorkload):
+    q = normal_f16(w.seed, STREAM_Q, (w.B, w.H, w.Sq, w.D))
+    k = normal_f16(w.seed + 1, STREAM_K, (w.B, w.H, w.Sk, w.D))
+    v = normal_f16(w.seed + 1, STREAM_V, (w.B, w.H, w.Sk, w.D))
+    return q, k, v
+
+
+# Decoding against a key/value cache (the Emmy comments page closes on it): one
+# new token for 8 sequences x 32 heads over an 8k-token cache at D = 128, and
+# 16 new tokens of one sequence x 8 heads over a 128k-token cache at D = 64.
+DECODE = {
+    "decode_b8h32q1k8192d128": CacheWorkload("decode_b8h32q1k8192d128", 8, 32, 1, 8192, 128,
+                                             True, SEED_BASE + 20),
+    "decode_b1h8q16k131072d64": CacheWorkload("decode_b1h8q16k131072d64", 1, 8, 16, 131072, 64,
+                                              True, SEED_BASE + 22),
+}

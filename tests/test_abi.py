@@ -209,3 +209,29 @@ def test_variant_refusals_on_host(name, kw, status):
                                a["D"], a["scale"], a["causal"], a["variant"], 0)
     assert _lib.STATUS_NAMES[rc] == status
     assert _lib.load().attn_last_error().decode()
+
+
+def _kv(Sq=4, Sk=100, n_splits=2, ws=W, ws_bytes=1 << 30, **kw):
+    a = dict(q=A, k=B_, v=C, o=O, lse=L, B=1, H=2, D=64, scale=0.125, causal=0)
+    a.update(kw)
+    return _lib.attn_fwd_kvcache(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], Sq, Sk,
+                                 a["D"], a["scale"], a["causal"], n_splits, ws, ws_bytes, 0)
+
+
+KV_INVALID = [
+    ("causal S_q > S_k", dict(Sq=9, Sk=8, causal=1), "ATTN_ERR_SHAPE"),
+    ("S_q = 0", dict(Sq=0), "ATTN_ERR_SHAPE"),
+    ("S_k = 0", dict(Sk=0), "ATTN_ERR_SHAPE"),
+    ("D=96", dict(D=96), "ATTN_ERR_UNSUPPORTED"),
+    ("n_splits=65", dict(n_splits=65), "ATTN_ERR_ARG"),
+    ("null workspace", dict(ws=0), "ATTN_ERR_NULL"),
+    ("short workspace", dict(ws_bytes=2 * 2 * 4 * 65 * 4 - 1), "ATTN_ERR_ARG"),
+    ("one head's cache too large", dict(Sk=1 << 24, D=128), "ATTN_ERR_SHAPE"),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", KV_INVALID, ids=[c[0] for c in KV_INVALID])
+def test_kvcache_invalid_arguments_are_rejected_on_host(name, kw, status):
+    rc = _kv(**kw)
+    assert _lib.STATUS_NAMES[rc] == status
+    assert _lib.load().attn_last_error().decode()
