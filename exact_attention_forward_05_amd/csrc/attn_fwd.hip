@@ -15,7 +15,7 @@
 static_assert(attn::BLOCK_M == attn::plan::BLOCK_M, "query tile of the kernel and of the plan");
 static_assert(attn::THREADS == attn::plan::THREADS, "workgroup size of the kernel and of the plan");
 static_assert(attn::VAR_RING3 == ATTN_VARIANT_RING3 && attn::VAR_EXP_POLY == ATTN_VARIANT_EXP_POLY &&
-                  attn::VAR_WIDE == ATTN_VARIANT_WIDE,
+                  attn::VAR_WIDE == ATTN_VARIANT_WIDE && attn::VAR_SUBPIPE == ATTN_VARIANT_SUBPIPE,
               "variant flags of the kernel and of the header");
 
 namespace {
@@ -96,6 +96,7 @@ int dispatch_variant(const void* q, const void* k, const void* v, void* o, float
       case VAR_RING3: return launch_variant<64, VAR_RING3>(q, k, v, o, lse, B, H, S, scale, causal, st);
       case VAR_EXP_POLY: return launch_variant<64, VAR_EXP_POLY>(q, k, v, o, lse, B, H, S, scale, causal, st);
       case VAR_WIDE: return launch_variant<64, VAR_WIDE>(q, k, v, o, lse, B, H, S, scale, causal, st);
+      case VAR_SUBPIPE: return launch_variant<64, VAR_SUBPIPE>(q, k, v, o, lse, B, H, S, scale, causal, st);
       default: break;
     }
   } else {
@@ -106,9 +107,9 @@ int dispatch_variant(const void* q, const void* k, const void* v, void* o, float
     }
   }
   return attn::plan::fail(msg(), ATTN_ERR_UNSUPPORTED,
-                          "kernel variant %d is not built for D=%d (D=64: 0, %d, %d, %d; "
+                          "kernel variant %d is not built for D=%d (D=64: 0, %d, %d, %d, %d; "
                           "D=128: 0, %d)", variant, D, ATTN_VARIANT_RING3, ATTN_VARIANT_EXP_POLY,
-                          ATTN_VARIANT_WIDE, ATTN_VARIANT_EXP_POLY);
+                          ATTN_VARIANT_WIDE, ATTN_VARIANT_SUBPIPE, ATTN_VARIANT_EXP_POLY);
 }
 
 // Checks shared by the entry points (Sq query rows against Sk keys).

@@ -10,19 +10,14 @@
 //
 // Work decomposition. A workgroup of 8 waves owns BLOCK_M = 128 query rows of
 // one (batch, head) and streams the keys in intervals of 128, which arrive in
-// LDS as NPH tiles of BN = 128 / NPH keys. The waves form QGROUPS = 8 / NPH
-// query groups of 128 / QGROUPS rows; the NPH waves of a group take one tile
-// each per interval (wave phase p folds tiles p, p + NPH, ...), so the two
-// waves on one SIMD work on independent data and fill each other's stalls.
-//   D = 64:  NPH = 4, 32-key tiles, 2 query groups of 64 rows (4 sub-tiles of
-//            16 rows per wave);
-//   D = 128: NPH = 2, 64-key tiles, 4 query groups of 32 rows (2 sub-tiles).
-// Each K or V fragment read from LDS feeds the MFMAs of all of a wave's rows,
-// so at D = 64 the 64-row waves halve the operand reads per MFMA (the MFMA
-// stream was limited by them with 32-row waves); at D = 128 the output
-// accumulators of 64 rows would not fit next to the rest. At the end the NPH
-// carriers of a query group meet in LDS and each wave merges them for its
-// share of the output columns.
+// LDS as NPH = 2 tiles of BN = 64 keys. The waves form QGROUPS = 4 query
+// groups of 32 rows (two 16-row sub-tiles per wave); the NPH waves of a group
+// take one tile each per interval (wave phase p folds tiles p, p + NPH, ...).
+// Wave w runs on SIMD w % 4, so the two waves on one SIMD hold different
+// query rows and fill each other's stalls. (VAR_WIDE at D = 64: NPH = 4
+// tiles of 32 keys, 2 query groups of 64 rows.) At the end the NPH carriers of
+// a query group meet in LDS and each wave merges them for its share of the
+// output columns.
 //
 // MFMA: v_mfma_f32_16x16x32_f16. Lane l = 16*g + i (g = 0..3, i = 0..15):
 //   A: row i, contraction slots (g, 0..7); B: column i, slots (g, 0..7);
@@ -88,6 +83,7 @@ enum : int {
   VAR_RING3 = 1,     // D = 64: three-slot K/V ring, copies two intervals ahead
   VAR_EXP_POLY = 2,  // one exponential in four by an FMA polynomial
   VAR_WIDE = 4,      // D = 64: 64-row waves over four 32-key tiles per interval
+  VAR_SUBPIPE = 8,   // D = 64: MFMAs of one sub-tile beside the softmax of the other
 };
 
 template <int D, int VAR = 0>
@@ -118,11 +114,12 @@ struct Geometry {
   // At D = 128 the Q fragments would not fit the register budget next to the
   // output accumulators: the workgroup's Q rows are staged in LDS instead.
   static constexpr bool Q_IN_LDS = D == 128;
-  // Odd waves run half an interval out of phase with even waves (softmax
-  // against the other wave's MFMA phase). This pays only where the MFMA phase
-  // is long next to the softmax: at D = 128 (5% on causal B2 H16 S8192), not
-  // at D = 64 (5% slower, and no faster with fp32-add row sums in place of
-  // the v_dot2 sums that wait for the other wave's MFMAs).
+  // The second wave of each SIMD (waves 4-7) runs half an interval out of
+  // phase with the first (softmax against the other wave's MFMA phase). This
+  // pays only where the MFMA phase is long next to the softmax: at D = 128
+  // (5% on causal B2 H16 S8192), not at D = 64 (5% slower, and no faster
+  // with fp32-add row sums in place of the v_dot2 sums that wait for the
+  // other wave's MFMAs).
   static constexpr bool PINGPONG = D == 128;
   // At D = 64 a tile's P.V runs in the same interval as its Q.K^T and
   // softmax (three phases, V copied one interval earlier): the SIMD's two
@@ -135,6 +132,14 @@ struct Geometry {
   static constexpr bool SOFTMAX_PRIO = true;
   // One exponential in four computed on the FMA path (VAR_EXP_POLY).
   static constexpr bool EXP_POLY = (VAR & VAR_EXP_POLY) != 0;
+  // Sub-tile pipelined interval (VAR_SUBPIPE, D = 64 with two sub-tiles):
+  // Q.K^T of sub-tile 1 runs beside the softmax of sub-tile 0, and P.V of
+  // sub-tile 0 beside the softmax of sub-tile 1, each pair in one scheduling
+  // region with SIDE_VPER VALU instructions after each MFMA. Measured 2-5%
+  // slower than the default order (3 VALU instructions per MFMA was the best
+  // of 3, 6, 10 and 16; fp32-add row sums in place of v_dot2 did not help).
+  static constexpr bool SUBPIPE = D == 64 && (VAR & VAR_SUBPIPE) != 0 && QSUB == 2;
+  static constexpr int SIDE_VPER = 3;
   static constexpr int Q_HALVES = Q_IN_LDS ? BLOCK_M * D : 0;
   static constexpr int D_CHUNKS = D / 32;                  // contraction chunks of Q.K
   static constexpr int D_BLOCKS = D / 16;                  // 16-row blocks of O^T
@@ -311,6 +316,7 @@ using ProbSet = f16x8[Geometry<D, VAR>::QSUB][Geometry<D, VAR>::KC];
 // Scheduling groups (sched_group_barrier masks): LDS reads and MFMAs.
 constexpr int SG_DS_READ = 0x100;
 constexpr int SG_MFMA = 0x008;
+constexpr int SG_VALU = 0x002;
 // LDS read instructions of unit u: two transposing reads for a V^T fragment,
 // one 16-byte read for a K fragment.
 template <int U, int END, int NPV>
@@ -428,6 +434,75 @@ __device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
   }
 }
 
+// Operand fragments of one tile for the sub-tile pipelined interval
+// (VAR_SUBPIPE): K fragments (unit ch * KB + kb) and V^T fragments (unit
+// kc * D_BLOCKS + db), read from LDS as in mfma_phase, then consumed by the
+// MFMAs of one sub-tile at a time.
+template <int D, int VAR>
+struct TileFrags {
+  f16x8 k[Geometry<D, VAR>::KB * Geometry<D, VAR>::D_CHUNKS];
+  f16x8 v[Geometry<D, VAR>::KC * Geometry<D, VAR>::D_BLOCKS];
+};
+
+template <int D, int VAR>
+__device__ __forceinline__ void read_k_frags(TileFrags<D, VAR>& fr,
+                                             const _Float16* __restrict__ ktile, int li, int g) {
+  using G = Geometry<D, VAR>;
+  const int ksw = k_swizzle<D>(li);
+#pragma unroll
+  for (int ch = 0; ch < G::D_CHUNKS; ++ch)
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb)
+      fr.k[ch * G::KB + kb] =
+          *reinterpret_cast<const f16x8*>(ktile + (16 * kb + li) * D + 8 * ((4 * ch + g) ^ ksw));
+}
+
+template <int D, int VAR>
+__device__ __forceinline__ void read_v_frags(TileFrags<D, VAR>& fr,
+                                             const _Float16* __restrict__ vtile, int li, int g) {
+  using G = Geometry<D, VAR>;
+  const int vrow = 8 * g + (li >> 2);
+  const int vsw = v_swizzle<D>(vrow);
+  const _Float16* vlane = vtile + vrow * D + 4 * (li & 1);
+  const int vx = (li & 3) >> 1;
+#pragma unroll
+  for (int kc = 0; kc < G::KC; ++kc)
+#pragma unroll
+    for (int db = 0; db < G::D_BLOCKS; ++db) {
+      const _Float16* vp = vlane + 8 * ((2 * db + vx) ^ vsw) + (32 * kc) * D;
+      const f16x4 lo = lds_read_tr(vp);
+      const f16x4 hi = lds_read_tr(vp + 4 * D);
+      fr.v[kc * G::D_BLOCKS + db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+// S^T of sub-tile QS from the K fragments and its Q^T fragments.
+template <int D, int VAR, int QS>
+__device__ __forceinline__ void qk_sub(ScoreSet<D, VAR>& sc, const TileFrags<D, VAR>& fr,
+                                       const QSet<D, VAR>& qf) {
+  using G = Geometry<D, VAR>;
+#pragma unroll
+  for (int ch = 0; ch < G::D_CHUNKS; ++ch)
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb)
+      sc[QS][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          fr.k[ch * G::KB + kb], qf[QS][ch], ch == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[QS][kb],
+          0, 0, 0);
+}
+
+// O^T += V^T . P^T of sub-tile QS.
+template <int D, int VAR, int QS>
+__device__ __forceinline__ void pv_sub(CarrierSet<D, VAR>& cr, const TileFrags<D, VAR>& fr,
+                                       const ProbSet<D, VAR>& pf) {
+  using G = Geometry<D, VAR>;
+#pragma unroll
+  for (int kc = 0; kc < G::KC; ++kc)
+#pragma unroll
+    for (int db = 0; db < G::D_BLOCKS; ++db)
+      cr[QS].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fr.v[kc * G::D_BLOCKS + db],
+                                                            pf[QS][kc], cr[QS].o[db], 0, 0, 0);
+}
+
 // 2^x on the FMA path (the exponential offload of the VAR_EXP_POLY variant,
 // after FlashAttention-4's emulated exponential; the coefficients are this
 // project's own fit). x is clamped to [-126, 127]: arguments above still
@@ -465,19 +540,42 @@ __device__ __forceinline__ f32x4 exp_block(f32x4 s, float c, float m, uint32_t h
 
 // Online softmax of one tile's scores: probabilities (fp16, P^T operand
 // layout) into pf, denominators and, when the max moves, outputs rescaled.
-template <int D, int VAR, bool CAUSAL, bool MASK>
+struct NoSide {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// Pins the side work's MFMAs between the softmax's VALU instructions of one
+// scheduling region: its LDS reads first, then each MFMA followed by VPER
+// VALU instructions.
+template <int VPER, int I, int N>
+__device__ __forceinline__ void pin_side_mfmas() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_VALU, VPER, 0);
+    pin_side_mfmas<VPER, I + 1, N>();
+  }
+}
+
+// Online softmax of sub-tiles [QS_LO, QS_HI) of a tile. SIDE_MFMAS > 0: the
+// `side` work (SIDE_READS LDS reads and SIDE_MFMAS MFMAs that do not touch
+// these sub-tiles) is issued in the same scheduling region, before the
+// lazy-max branch, and interleaved with the softmax's VALU instructions.
+template <int D, int VAR, bool CAUSAL, bool MASK, int QS_LO = 0, int QS_HI = -1,
+          int SIDE_MFMAS = 0, int SIDE_READS = 0, class Side = NoSide>
 __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
                                              const ScoreSet<D, VAR>& sc,
                                              ProbSet<D, VAR>& pf, float c, int key0,
-                                             int qpos0, int S, int li, int g) {
+                                             int qpos0, int S, int li, int g,
+                                             Side&& side = Side{}) {
   using G = Geometry<D, VAR>;
-  constexpr int QSUB = G::QSUB;
+  constexpr int QSUB = QS_HI < 0 ? G::QSUB : QS_HI;  // one past the last sub-tile
+  side();
   // hidden-key bits per sub-tile and key block (bit r: accumulator element
   // r): keys past S, and (causal) keys after the query's sequence position
   // (qpos0 is the position of the wave's first row)
   uint32_t hid[QSUB][G::KB];
 #pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs)
+  for (int qs = QS_LO; qs < QSUB; ++qs)
 #pragma unroll
     for (int kb = 0; kb < G::KB; ++kb) {
       hid[qs][kb] = 0u;
@@ -526,7 +624,11 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
       tsum[qs] = acc[0] + acc[1];
   };
 #pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs) expo(qs);
+  for (int qs = QS_LO; qs < QSUB; ++qs) expo(qs);
+  if constexpr (SIDE_MFMAS > 0) {
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, SIDE_READS, 0);
+    pin_side_mfmas<G::SIDE_VPER, 0, SIDE_MFMAS>();
+  }
   // Lazy max: refresh m only when this tile's probabilities could overflow,
   // and only for the sub-tiles whose lanes exceed the bound (one test on the
   // common path; with peaked scores one row in 256 often trips it, and every
@@ -536,10 +638,10 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
   };
   bool over = false;
 #pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs) over = over || big(qs);
+  for (int qs = QS_LO; qs < QSUB; ++qs) over = over || big(qs);
   if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
-    for (int qs = 0; qs < QSUB; ++qs) {
+    for (int qs = QS_LO; qs < QSUB; ++qs) {
       if (__builtin_amdgcn_ballot_w64(big(qs)) == 0) continue;
       float tmax = NEG_BIG;
 #pragma unroll
@@ -562,22 +664,26 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
     }
   }
 #pragma unroll
-  for (int qs = 0; qs < QSUB; ++qs) cr[qs].d = SUM_ONTO_D ? dnew[qs] : cr[qs].d + tsum[qs];
+  for (int qs = QS_LO; qs < QSUB; ++qs) cr[qs].d = SUM_ONTO_D ? dnew[qs] : cr[qs].d + tsum[qs];
 }
 
-template <int D, int VAR, bool CAUSAL>
+template <int D, int VAR, bool CAUSAL, int QS_LO = 0, int QS_HI = -1, int SIDE_MFMAS = 0,
+          int SIDE_READS = 0, class Side = NoSide>
 __device__ __forceinline__ void softmax_any(CarrierSet<D, VAR>& cr,
                                             const ScoreSet<D, VAR>& sc,
                                             ProbSet<D, VAR>& pf, float c, int key0,
-                                            int qpos0, int S, int li, int g) {
+                                            int qpos0, int S, int li, int g,
+                                            Side&& side = Side{}) {
   constexpr int BN = Geometry<D, VAR>::BN;
   // Element masks are needed on the sequence tail and on tiles reaching past
   // the position of the wave's first query (causal diagonal).
   const bool needs_mask = (key0 + BN > S) || (CAUSAL && key0 + BN - 1 > qpos0);
   if (needs_mask)
-    softmax_tile<D, VAR, CAUSAL, true>(cr, sc, pf, c, key0, qpos0, S, li, g);
+    softmax_tile<D, VAR, CAUSAL, true, QS_LO, QS_HI, SIDE_MFMAS, SIDE_READS>(
+        cr, sc, pf, c, key0, qpos0, S, li, g, side);
   else
-    softmax_tile<D, VAR, CAUSAL, false>(cr, sc, pf, c, key0, qpos0, S, li, g);
+    softmax_tile<D, VAR, CAUSAL, false, QS_LO, QS_HI, SIDE_MFMAS, SIDE_READS>(
+        cr, sc, pf, c, key0, qpos0, S, li, g, side);
 }
 
 // Workgroup id -> (batch*head, query tiles) by `order` (work_order.h).
@@ -636,8 +742,11 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const int lane = tid & 63;
     const int li = lane & 15;
     const int g = lane >> 4;
-    const int qgrp = wave % G::QGROUPS;
-    const int phase = wave / G::QGROUPS;
+    // The NPH waves of a query group are consecutive, so that they run on
+    // different SIMDs: when only the first query group has live rows (a few
+    // queries against a long cache) its waves do not share a SIMD.
+    const int qgrp = wave / NPH;
+    const int phase = wave % NPH;
     const bool late = wave >= WAVES / 2;  // second wave of its SIMD
     const int q0 = qt * BLOCK_M;
     const int qrow0 = q0 + G::ROWS * qgrp;  // this wave's first query row
@@ -802,9 +911,61 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
           wait_copies();
         __syncthreads();
       };
+      // Sub-tile pipelined interval (SUBPIPE): Q.K^T of sub-tile 0; then Q.K^T
+      // of sub-tile 1 and the V^T reads beside the softmax of sub-tile 0; then
+      // P.V of sub-tile 0 beside the softmax of sub-tile 1; then P.V of
+      // sub-tile 1. Each softmax ends with its own lazy-max branch, so the
+      // MFMAs beside it never depend on a redo.
+      auto softmax_sub = [&](int jj, auto edge_flag, auto qs_flag, auto nside, auto nread,
+                             auto&& side) __attribute__((always_inline)) {
+        constexpr int QS = decltype(qs_flag)::value;
+        constexpr int NS = decltype(nside)::value;
+        constexpr int NR = decltype(nread)::value;
+        const int key0 = (pb + jj) * INTERVAL_KEYS + phase * G::BN;
+        if constexpr (decltype(edge_flag)::value)
+          softmax_any<D, VAR, CAUSAL, QS, QS + 1, NS, NR>(cr, sc, pf, c, key0, qpos0, S, li, g,
+                                                          side);
+        else
+          softmax_tile<D, VAR, CAUSAL, false, QS, QS + 1, NS, NR>(cr, sc, pf, c, key0, qpos0, S,
+                                                                  li, g, side);
+      };
+      auto full_sp = [&](int jj, auto edge_flag, auto slot_flag) __attribute__((always_inline)) {
+        if constexpr (G::SUBPIPE) {
+          constexpr int SL = decltype(slot_flag)::value;
+          const int slot = SL >= 0 ? SL : jj % R;
+          const _Float16* kslot = kring + slot * G::SLOT_HALVES + phase * G::K_HALVES;
+          const _Float16* vslot = vring + slot * G::SLOT_HALVES + phase * G::V_HALVES;
+          using I0 = std::integral_constant<int, 0>;
+          using I1 = std::integral_constant<int, 1>;
+          using NQK = std::integral_constant<int, G::KB * G::D_CHUNKS>;
+          using NPV = std::integral_constant<int, G::KC * G::D_BLOCKS>;
+          using NVR = std::integral_constant<int, 2 * G::KC * G::D_BLOCKS>;
+          TileFrags<D, VAR> fr;
+          read_k_frags<D, VAR>(fr, kslot, li, g);
+          qk_sub<D, VAR, 0>(sc, fr, qf);
+          __builtin_amdgcn_sched_barrier(0);
+          copies_ahead(jj);
+          __builtin_amdgcn_sched_barrier(0);
+          softmax_sub(jj, edge_flag, I0{}, NQK{}, NVR{}, [&]() __attribute__((always_inline)) {
+            qk_sub<D, VAR, 1>(sc, fr, qf);
+            read_v_frags<D, VAR>(fr, vslot, li, g);
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          softmax_sub(jj, edge_flag, I1{}, NPV{}, I0{}, [&]() __attribute__((always_inline)) {
+            pv_sub<D, VAR, 0>(cr, fr, pf);
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          pv_sub<D, VAR, 1>(cr, fr, pf);
+          end_int(jj);
+        }
+      };
       // slot_flag: the ring slot of interval jj as a compile-time constant,
       // or -1 to take it from jj at run time.
       auto full = [&](int jj, auto edge_flag, auto slot_flag) __attribute__((always_inline)) {
+        if constexpr (G::SUBPIPE) {
+          full_sp(jj, edge_flag, slot_flag);
+          return;
+        }
         constexpr int SL = decltype(slot_flag)::value;
         const int slot = SL >= 0 ? SL : jj % R;
         const _Float16* kslot = kring + slot * G::SLOT_HALVES + phase * G::K_HALVES;
@@ -930,7 +1091,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       float m = NEG_BIG;
   #pragma unroll
       for (int p = 0; p < NPH; ++p) {
-        const f32x4 md = *md_slot(p * G::QGROUPS + qgrp, qs);
+        const f32x4 md = *md_slot(qgrp * NPH + p, qs);
         mp[p] = md[(qs & 1) * 2];
         dp[p] = md[(qs & 1) * 2 + 1];
         m = __builtin_fmaxf(m, mp[p]);
@@ -958,7 +1119,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
             if (p == db / G::OWN_DB)
               acc += cr[qs].o[db] * w[p];
             else
-              acc += *o_slot(p * G::QGROUPS + qgrp, qs, db) * w[p];
+              acc += *o_slot(qgrp * NPH + p, qs, db) * w[p];
           }
           if constexpr (SPLIT) {
             float* po = part_o + (part_row0 + row) * D;

@@ -121,6 +121,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                                  /* issued two key intervals ahead of their use  */
 #define ATTN_VARIANT_EXP_POLY 2  /* one exponential in four on the FMA path     */
 #define ATTN_VARIANT_WIDE 4      /* D = 64: 64-row waves over four 32-key tiles  */
+#define ATTN_VARIANT_SUBPIPE 8   /* D = 64: the two 16-row sub-tiles of a wave   */
+                                 /* pipelined against each other in one interval */
 
 /*
  * attn_fwd_variant -- attn_fwd with a chosen compiled variant of the kernel,
@@ -134,10 +136,15 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *    FA-3 and FA-4: FlashAttention-4's emulated exponential).
  *  - ATTN_VARIANT_WIDE: each wave owns 64 query rows instead of 32, halving
  *    the LDS operand reads per MFMA (Part 2, Move 4: register tiling).
+ *  - ATTN_VARIANT_SUBPIPE: within a wave, the Q.K^T of its second 16-row
+ *    sub-tile and the P.V of its first are scheduled beside the softmax of
+ *    the other sub-tile, so the matrix and vector units of one wave overlap
+ *    (Part 2, Relationship to FA-3 and FA-4: overlapping the softmax with
+ *    the matrix products).
  *
  *  q ... causal, stream : as attn_fwd (same layouts, checks and status codes).
  *  variant : one of the ATTN_VARIANT_* values; D = 64 builds 0, RING3,
- *            EXP_POLY and WIDE, D = 128 builds 0 and EXP_POLY. Any other
+ *            EXP_POLY, WIDE and SUBPIPE, D = 128 builds 0 and EXP_POLY. Any other
  *            value (or combination) returns ATTN_ERR_UNSUPPORTED before
  *            anything is enqueued.
  */

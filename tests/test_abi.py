@@ -195,7 +195,8 @@ VARIANT_REFUSED = [
     ("D128 ring3", dict(D=128, variant=1), "ATTN_ERR_UNSUPPORTED"),
     ("D128 wide", dict(D=128, variant=4), "ATTN_ERR_UNSUPPORTED"),
     ("combined flags", dict(variant=3), "ATTN_ERR_UNSUPPORTED"),
-    ("unknown flag", dict(variant=8), "ATTN_ERR_UNSUPPORTED"),
+    ("D128 subpipe", dict(D=128, variant=8), "ATTN_ERR_UNSUPPORTED"),
+    ("unknown flag", dict(variant=16), "ATTN_ERR_UNSUPPORTED"),
     ("negative", dict(variant=-1), "ATTN_ERR_UNSUPPORTED"),
     ("arguments checked first", dict(variant=99, q=0), "ATTN_ERR_NULL"),
 ]

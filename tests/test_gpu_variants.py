@@ -16,8 +16,8 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 # (D, variant) pairs built into the library, besides the default kernel
-BUILT = [(64, 1), (64, 2), (64, 4), (128, 2)]
-NAMES = {1: "ring3", 2: "exp_poly", 4: "wide"}
+BUILT = [(64, 1), (64, 2), (64, 4), (64, 8), (128, 2)]
+NAMES = {1: "ring3", 2: "exp_poly", 4: "wide", 8: "subpipe"}
 
 SHAPES = [
     # B, H, S, causal, scale, seed
