@@ -111,8 +111,7 @@ struct Launch {
 
 // Launch geometry of one call; ATTN_ERR_SHAPE if a grid does not fit a
 // dispatch. Arguments are already checked.
-inline int make_launch(int B, int H, int Sq, int D, int causal, int n_splits, Launch* out,
-                       Msg m) {
+inline int make_launch(int B, int H, int Sq, int causal, int n_splits, Launch* out, Msg m) {
   const int64_t BH = (int64_t)B * H;
   const int n_qtiles = (int)(((int64_t)Sq + BLOCK_M - 1) / BLOCK_M);
   // Single pass: non-causal work is uniform, so the order serves L2 locality
@@ -135,8 +134,8 @@ inline int make_launch(int B, int H, int Sq, int D, int causal, int n_splits, La
                 (long long)blocks, THREADS);
   int64_t cblocks = 0;
   if (n_splits > 1) {
-    const int64_t items = BH * Sq * (D / 4);  // one thread per row and 4 columns
-    cblocks = (items + COMBINE_THREADS - 1) / COMBINE_THREADS;
+    const int64_t rows_per_block = COMBINE_THREADS / 64;  // one wave per row
+    cblocks = (BH * Sq + rows_per_block - 1) / rows_per_block;
     if (cblocks > COMBINE_MAX_BLOCKS) cblocks = COMBINE_MAX_BLOCKS;
   }
   out->order = order;

@@ -114,7 +114,7 @@ int main() {
             const int B = (int)(BH >= 4 ? BH / 4 : BH), H = (int)(BH >= 4 ? 4 : 1);
             plan::Launch L{};
             buf[0] = '\0';
-            const int rc = plan::make_launch(B, H, S, D, causal, ns, &L, m);
+            const int rc = plan::make_launch(B, H, S, causal, ns, &L, m);
             ++launches;
             const int64_t nq = (S + 127) / 128;
             const int64_t per_head = L.order == ORDER_FOLDED ? (nq + 1) / 2 : nq;
