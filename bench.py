@@ -54,6 +54,9 @@ def parse():
                     help="timed launches per sweep point")
     ap.add_argument("--cold", action="store_true",
                     help="also time launches with caches flushed (512 MB written before each)")
+    ap.add_argument("--decode", default=None, metavar="WORKLOAD",
+                    help="time only this key/value-cache (decode) workload and print its "
+                         "record (for profiler runs)")
     return ap.parse_args()
 
 
@@ -389,7 +392,7 @@ def run_variants(attn, dev, stream, steps, prewarm_ms):
     return out
 
 
-def run_decode(attn, dev, stream, steps, prewarm_ms):
+def run_decode(attn, dev, stream, steps, prewarm_ms, names=None):
     """Queries against a key/value cache (attn_fwd_kvcache, split count from
     the library's model): kernel time of the split pass plus the combine,
     against the HBM roofline (K and V read once dominate the bytes)."""
@@ -400,6 +403,8 @@ def run_decode(attn, dev, stream, steps, prewarm_ms):
 
     out = []
     for name, w in DECODE.items():
+        if names is not None and name not in names:
+            continue
         q, k, v = (torch.from_numpy(x).to(dev) for x in cache_inputs(w))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
@@ -438,6 +443,21 @@ def run_decode(attn, dev, stream, steps, prewarm_ms):
     return out
 
 
+def copy_calibration(dev):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
+    calibrate the HBM byte counters read for the attention kernels."""
+    import torch
+
+    nbytes = 256 << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    log(f"copy calibration: 3 copies of {nbytes} bytes")
+    del src, dst
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -451,10 +471,21 @@ def main():
     import torch
 
     import exact_attention_forward_05_amd as attn
-    from testkit import HEADLINE, WORKLOADS, workload_inputs
+    from testkit import DECODE, HEADLINE, WORKLOADS, workload_inputs
 
-    w = WORKLOADS[args.workload or HEADLINE]
     dev = torch.device("cuda:0")
+    if args.decode is not None:
+        if args.decode not in DECODE:
+            print(json.dumps({"error": f"unknown decode workload {args.decode}",
+                              "choices": sorted(DECODE)}))
+            sys.exit(2)
+        recs = run_decode(attn, dev, torch.cuda.current_stream(dev), args.steps,
+                          args.prewarm_ms, names=(args.decode,))
+        if args.copy_calibration:  # after the inputs' host-to-device copies
+            copy_calibration(dev)
+        print(json.dumps({"decode": recs[0]}))
+        return
+    w = WORKLOADS[args.workload or HEADLINE]
     props = torch.cuda.get_device_properties(dev)
     log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
     log(f"workload {w.name}: {w.describe()}")
@@ -471,16 +502,7 @@ def main():
     step = raw_step("attn_fwd", qt, kt, vt, o, lse, w, stream)
 
     if args.copy_calibration:
-        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
-        # calibrate the HBM byte counters read for the attention kernel.
-        nbytes = 256 << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize(dev)
-        log(f"copy calibration: 3 copies of {nbytes} bytes")
-        del src, dst
+        copy_calibration(dev)
 
     pre = prewarm(step, args.prewarm_ms)
     log(f"prewarm: {pre['steps']} launches in {pre['ms']} ms")

@@ -15,6 +15,7 @@
 static_assert(attn::BLOCK_M == attn::plan::BLOCK_M, "query tile of the kernel and of the plan");
 static_assert(attn::THREADS == attn::plan::THREADS, "workgroup size of the kernel and of the plan");
 static_assert(attn::COMBINE_THREADS == attn::plan::COMBINE_THREADS, "combine workgroup size");
+static_assert(attn::MAX_SPLITS == ATTN_MAX_SPLITS, "split limit of the kernel and of the header");
 static_assert(attn::VAR_RING3 == ATTN_VARIANT_RING3 && attn::VAR_EXP_POLY == ATTN_VARIANT_EXP_POLY &&
                   attn::VAR_WIDE == ATTN_VARIANT_WIDE && attn::VAR_SUBPIPE == ATTN_VARIANT_SUBPIPE,
               "variant flags of the kernel and of the header");
@@ -31,7 +32,7 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
            int Sq, int Sk, float scale, int n_splits, void* workspace, hipStream_t stream) {
   using namespace attn;
   plan::Launch L;
-  const int rc = plan::make_launch(B, H, Sq, CAUSAL ? 1 : 0, n_splits, &L, msg());
+  const int rc = plan::make_launch(B, H, Sq, D, CAUSAL ? 1 : 0, n_splits, &L, msg());
   if (rc != ATTN_OK) return rc;
   const int BH = B * H;
   // Scores are folded in base 2: t = s * |scale| * log2(e). A negative scale
@@ -57,9 +58,14 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (err != hipSuccess)
       return plan::fail(msg(), ATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     const int64_t rows = (int64_t)BH * Sq;
-    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)L.combine_blocks),
-                       dim3(plan::COMBINE_THREADS), 0, stream, part_o, part_lse, oh, lse, rows,
-                       n_splits);
+    if (L.combine_runs)
+      hipLaunchKernelGGL((attn_combine_runs_kernel<D>), dim3((unsigned)L.combine_blocks),
+                         dim3(plan::COMBINE_THREADS), 0, stream, part_o, part_lse, oh, lse, rows,
+                         n_splits);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)L.combine_blocks),
+                         dim3(plan::COMBINE_THREADS), 0, stream, part_o, part_lse, oh, lse, rows,
+                         n_splits);
   }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess)
@@ -124,7 +130,7 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
   if (n_splits > 1 && attn::plan::workspace_size(B, H, Sq, D, n_splits) == 0)
     return attn::plan::fail(msg(), ATTN_ERR_SHAPE, "workspace size overflows");
   attn::plan::Launch L;  // grid limits, checked before anything is enqueued
-  return attn::plan::make_launch(B, H, Sq, causal, n_splits, &L, msg());
+  return attn::plan::make_launch(B, H, Sq, D, causal, n_splits, &L, msg());
 }
 
 // The workspace checks of the split entry points (n_splits > 1).

@@ -72,6 +72,7 @@ constexpr int WAVES = 8;              // waves per workgroup, two per SIMD
 constexpr int THREADS = WAVES * 64;
 constexpr int INTERVAL_KEYS = 128;    // keys per barrier interval
 constexpr int COMBINE_THREADS = 256;  // combine kernel: four waves, one row each
+constexpr int MAX_SPLITS = 64;        // key runs per query tile of a split launch, at most
 constexpr float NEG_BIG = -1.0e30f;   // finite stand-in for -infinity
 // Lazy-max bound on a lane's tile sum: every probability stays below it, and
 // so below fp16's largest finite value (65504) with room for rounding.
@@ -1155,38 +1156,93 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
 // Merge of the split-KV partial results (the carrier merge law, with each
 // run's state given as o_s = o/d and l_s = m + log2 d): for every row,
 // M = max_s l_s, w_s = 2^(l_s - M), O = sum_s w_s o_s / sum_s w_s and
-// LSE = (M + log2 sum_s w_s) ln 2. One wave per row: lane 16g + i reads
-// columns [CW i, CW i + CW) (CW = D / 16) of the runs s = g, g + 4, ..., so
-// that a row's runs are read in parallel (a decode launch has few rows and
-// many runs); the four lane groups' sums then meet by lane swaps. The grid
-// strides over the rows, so any row count fits a bounded grid.
+// LSE = (M + log2 sum_s w_s) ln 2. Two forms, chosen by the launch plan:
+//
+// attn_combine_kernel: one thread per row and 4 columns, the runs in turn.
+// Reads and writes are contiguous along the row; for launches with many rows
+// (prefill) it is HBM-bound.
 template <int D>
 __global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    _Float16* __restrict__ o, float* __restrict__ lse, int64_t rows, int n_splits) {
+  constexpr int TPR = D / 4;  // threads per row
+  const int64_t items = rows * TPR;
+  for (int64_t t = (int64_t)blockIdx.x * COMBINE_THREADS + threadIdx.x; t < items;
+       t += (int64_t)gridDim.x * COMBINE_THREADS) {
+    const int64_t row = t / TPR;
+    const int c4 = (int)(t % TPR);
+    float M = NEG_BIG;
+    for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, part_lse[s * rows + row]);
+    float W = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < n_splits; ++s) {
+      const float w = __builtin_amdgcn_exp2f(part_lse[s * rows + row] - M);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + (s * rows + row) * D + 4 * c4);
+      W += w;
+      acc += w * v;
+    }
+    const float inv = 1.0f / W;
+    f16x4 h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = (_Float16)(acc[r] * inv);
+    *reinterpret_cast<f16x4*>(o + row * D + 4 * c4) = h;
+    if (c4 == 0) lse[row] = (M + log2f(W)) * 0.69314718055994530942f;
+  }
+}
+
+// attn_combine_runs_kernel: one wave per row, for launches with few rows and
+// many runs (decode), where the form above would wait on one run after
+// another. Lane 16g + i holds
+// columns [CW i, CW i + CW) (CW = D / 16) of the runs s = g, g + 4, ..., all
+// loaded at once, so that the merge is one round trip of loads; the four lane
+// groups' maxima and sums then meet by lane swaps.
+//
+// Both grids stride over the rows, so any row count fits a bounded grid.
+template <int D>
+__global__ __launch_bounds__(COMBINE_THREADS) void attn_combine_runs_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
     _Float16* __restrict__ o, float* __restrict__ lse, int64_t rows, int n_splits) {
   constexpr int CW = D / 16;  // columns per lane
   constexpr int NV = CW / 4;  // f32x4 loads per lane and run
   constexpr int WPB = COMBINE_THREADS / 64;
+  constexpr int RUNS = (MAX_SPLITS + 3) / 4;  // runs per lane group, at most
   const int lane = threadIdx.x & 63;
   const int li = lane & 15;
   const int g = lane >> 4;
   const int64_t first = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
   for (int64_t row = first; row < rows; row += (int64_t)gridDim.x * WPB) {
-    float M = NEG_BIG;
-    for (int s = lane; s < n_splits; s += 64) M = __builtin_fmaxf(M, part_lse[s * rows + row]);
+    float l[RUNS];
+    f32x4 po[RUNS][NV];
 #pragma unroll
-    for (int x = 1; x < 64; x <<= 1) M = __builtin_fmaxf(M, __shfl_xor(M, x, 64));
+    for (int i = 0; i < RUNS; ++i) {
+      const int s = g + 4 * i;
+      if (s < n_splits) {
+        l[i] = part_lse[s * rows + row];
+        const float* src = part_o + (s * rows + row) * D + CW * li;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) po[i][v] = *reinterpret_cast<const f32x4*>(src + 4 * v);
+      } else {
+        l[i] = NEG_BIG;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) po[i][v] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+    float M = NEG_BIG;
+#pragma unroll
+    for (int i = 0; i < RUNS; ++i) M = __builtin_fmaxf(M, l[i]);
+    M = group_max(M);
     float W = 0.0f;
     f32x4 acc[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-    for (int s = g; s < n_splits; s += 4) {
-      const float w = __builtin_amdgcn_exp2f(part_lse[s * rows + row] - M);
-      const float* src = part_o + (s * rows + row) * D + CW * li;
+#pragma unroll
+    for (int i = 0; i < RUNS; ++i) {
+      // runs past n_splits, and runs with no visible key, have l = NEG_BIG:
+      // weight 0 against the finite M of a run that saw key 0
+      const float w = __builtin_amdgcn_exp2f(l[i] - M);
       W += w;
 #pragma unroll
-      for (int v = 0; v < NV; ++v) acc[v] += w * *reinterpret_cast<const f32x4*>(src + 4 * v);
+      for (int v = 0; v < NV; ++v) acc[v] += w * po[i][v];
     }
     W = group_sum(W);
 #pragma unroll

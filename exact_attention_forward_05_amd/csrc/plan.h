@@ -20,6 +20,7 @@ constexpr int BLOCK_M = 128;          // query rows per workgroup of the attenti
 constexpr int THREADS = 512;          // threads per workgroup of the attention kernel
 constexpr int COMBINE_THREADS = 256;  // threads per workgroup of the combine kernel
 constexpr int64_t COMBINE_MAX_BLOCKS = 1 << 16;  // the combine kernel strides over rows
+constexpr int64_t COMBINE_FILL_THREADS = 256 * 256;  // threads that fill 256 CUs once
 // Causal launches are folded (ORDER_FOLDED) from this many workgroups on:
 // the CU count of MI355X, one workgroup per CU.
 constexpr int64_t FOLD_MIN_WORKGROUPS = 256;
@@ -107,11 +108,13 @@ struct Launch {
   int n_qtiles;            // query tiles per head
   int64_t blocks;          // workgroups of the attention kernel
   int64_t combine_blocks;  // workgroups of the combine kernel (n_splits > 1), else 0
+  int combine_runs;        // 1: the wave-per-row combine (few rows), 0: thread per row
 };
 
 // Launch geometry of one call; ATTN_ERR_SHAPE if a grid does not fit a
 // dispatch. Arguments are already checked.
-inline int make_launch(int B, int H, int Sq, int causal, int n_splits, Launch* out, Msg m) {
+inline int make_launch(int B, int H, int Sq, int D, int causal, int n_splits, Launch* out,
+                       Msg m) {
   const int64_t BH = (int64_t)B * H;
   const int n_qtiles = (int)(((int64_t)Sq + BLOCK_M - 1) / BLOCK_M);
   // Single pass: non-causal work is uniform, so the order serves L2 locality
@@ -132,16 +135,25 @@ inline int make_launch(int B, int H, int Sq, int causal, int n_splits, Launch* o
   if (blocks * THREADS > MAX_WORK_ITEMS)
     return fail(m, ATTN_ERR_SHAPE, "grid of %lld workgroups x %d threads exceeds 2^32 work-items",
                 (long long)blocks, THREADS);
+  // Combine: with a thread per row and 4 columns, a launch whose threads do
+  // not fill the CUs once (few rows: decode) would merge its runs one after
+  // another; it takes a wave per row instead, all runs loaded at once.
   int64_t cblocks = 0;
+  int runs = 0;
   if (n_splits > 1) {
-    const int64_t rows_per_block = COMBINE_THREADS / 64;  // one wave per row
-    cblocks = (BH * Sq + rows_per_block - 1) / rows_per_block;
+    const int64_t rows = BH * Sq;
+    const int64_t threads = rows * (D / 4);
+    runs = threads < COMBINE_FILL_THREADS ? 1 : 0;
+    const int64_t per_block = runs ? COMBINE_THREADS / 64 : COMBINE_THREADS;
+    const int64_t items = runs ? rows : threads;
+    cblocks = (items + per_block - 1) / per_block;
     if (cblocks > COMBINE_MAX_BLOCKS) cblocks = COMBINE_MAX_BLOCKS;
   }
   out->order = order;
   out->n_qtiles = n_qtiles;
   out->blocks = blocks;
   out->combine_blocks = cblocks;
+  out->combine_runs = runs;
   return ATTN_OK;
 }
 

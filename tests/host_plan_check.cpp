@@ -4,6 +4,7 @@
 // workspace sizes against their closed form, grid sizes within one dispatch
 // (blocks * threads < 2^32, bounded combine grid) or ATTN_ERR_SHAPE, and
 // messages that stay inside a short buffer.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -114,7 +115,7 @@ int main() {
             const int B = (int)(BH >= 4 ? BH / 4 : BH), H = (int)(BH >= 4 ? 4 : 1);
             plan::Launch L{};
             buf[0] = '\0';
-            const int rc = plan::make_launch(B, H, S, causal, ns, &L, m);
+            const int rc = plan::make_launch(B, H, S, D, causal, ns, &L, m);
             ++launches;
             const int64_t nq = (S + 127) / 128;
             const int64_t per_head = L.order == ORDER_FOLDED ? (nq + 1) / 2 : nq;
@@ -128,6 +129,20 @@ int main() {
                                 L.combine_blocks <= plan::COMBINE_MAX_BLOCKS),
                     "combine grid %lld\n", (long long)L.combine_blocks);
               CHECK(ns > 1 || L.combine_blocks == 0, "combine grid without splits\n");
+              if (ns > 1) {
+                // wave-per-row combine exactly when a thread per row and 4
+                // columns would not fill the CUs once; the grid covers every
+                // row (or is capped and strides)
+                const int64_t rows = (int64_t)B * H * S;
+                const bool runs = rows * (D / 4) < plan::COMBINE_FILL_THREADS;
+                CHECK(L.combine_runs == (runs ? 1 : 0), "combine form\n");
+                const int64_t per = runs ? plan::COMBINE_THREADS / 64 : plan::COMBINE_THREADS;
+                const int64_t items = runs ? rows : rows * (D / 4);
+                const int64_t want = std::min<int64_t>((items + per - 1) / per,
+                                                       plan::COMBINE_MAX_BLOCKS);
+                CHECK(L.combine_blocks == want, "combine blocks %lld vs %lld\n",
+                      (long long)L.combine_blocks, (long long)want);
+              }
               CHECK(ns == 1 || L.order == ORDER_TILES, "split launches use ORDER_TILES\n");
               CHECK(causal || ns > 1 || L.order == ORDER_HEADS, "non-causal order\n");
             } else {

@@ -51,6 +51,10 @@ CASES = [
     (2, 2, 257, 128, True, 0.08838834764831845, 3, 7),
     (1, 1, 1000, 128, True, 0.08838834764831845, 5, 8),
     (1, 2, 333, 128, False, 0.5, 16, 9),       # peaked rows, many empty runs
+    # enough rows that the combine takes a thread per row and 4 columns
+    # (the cases above take a wave per row)
+    (1, 4, 1100, 64, True, 0.125, 3, 10),
+    (1, 2, 1100, 128, False, 0.08838834764831845, 2, 11),
 ]
 
 
