@@ -823,17 +823,29 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     // fall to different phases. (The last live interval of a split run is
     // checked at run time.)
 
+    // Key order. Loop step x folds the keys at interval position pos(x). In
+    // a non-causal single pass over whole intervals every wave's live
+    // intervals are all of them and none needs a mask, so the order is free:
+    // there, every other round of 32 workgroups per XCD (workgroup ids are
+    // dealt round-robin to 8 XCDs) walks the keys backwards and starts on the
+    // K/V that the round before it left in the XCD's L2 (at B1 H8 S16384 D64
+    // the fetched bytes halve). Elsewhere the order is ascending, as the
+    // peeled loop below assumes.
+    const bool backwards = !CAUSAL && !SPLIT && Sk % INTERVAL_KEYS == 0 &&
+                           ((blockIdx.x >> 8) & 1u) != 0u;
+    auto pos = [&](int x) { return pb + (backwards ? n_int - 1 - x : x); };
+
     CopyPlan<D> cp;
     make_copy_plan<D>(cp, wave, lane);
-    if (n_int > 0) copy_group<D>(cp.k_off, kh, pb * INTERVAL_KEYS, S, kring, wave);  // K of interval pb
+    if (n_int > 0) copy_group<D>(cp.k_off, kh, pos(0) * INTERVAL_KEYS, S, kring, wave);  // K of step 0
     if constexpr (G::PV_SAME) {
-      if (n_int > 0) copy_group<D>(cp.v_off, vh, pb * INTERVAL_KEYS, S, vring, wave);  // V of interval pb
+      if (n_int > 0) copy_group<D>(cp.v_off, vh, pos(0) * INTERVAL_KEYS, S, vring, wave);  // V of step 0
     }
     if constexpr (G::PV_SAME && R == 3) {
-      // three-slot ring: interval pb + 1 is in flight from the start
+      // three-slot ring: step 1 is in flight from the start
       if (n_int > 1) {
-        copy_group<D>(cp.k_off, kh, (pb + 1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, wave);
-        copy_group<D>(cp.v_off, vh, (pb + 1) * INTERVAL_KEYS, S, vring + G::SLOT_HALVES, wave);
+        copy_group<D>(cp.k_off, kh, pos(1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, wave);
+        copy_group<D>(cp.v_off, vh, pos(1) * INTERVAL_KEYS, S, vring + G::SLOT_HALVES, wave);
         wait_copies_keep<2 * G::LOADS>();
       } else {
         wait_copies();
@@ -855,16 +867,16 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     // branches.
     auto copies = [&](int j) __attribute__((always_inline)) {
       if (j + 1 < n_int)
-        copy_group<D>(cp.k_off, kh, (pb + j + 1) * INTERVAL_KEYS, S,
+        copy_group<D>(cp.k_off, kh, pos(j + 1) * INTERVAL_KEYS, S,
                       kring + ((j + 1) & 1) * G::SLOT_HALVES, wave);
       if (j < n_int)
-        copy_group<D>(cp.v_off, vh, (pb + j) * INTERVAL_KEYS, S,
+        copy_group<D>(cp.v_off, vh, pos(j) * INTERVAL_KEYS, S,
                       vring + (j & 1) * G::SLOT_HALVES, wave);
     };
     // softmax of this wave's tile of interval p (masks possible when EDGE)
     auto softmax_int = [&](int p, auto edge_flag) __attribute__((always_inline)) {
       if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(2);
-      const int key0 = (pb + p) * INTERVAL_KEYS + phase * G::BN;
+      const int key0 = pos(p) * INTERVAL_KEYS + phase * G::BN;
       if constexpr (decltype(edge_flag)::value)
         softmax_any<D, VAR, CAUSAL>(cr, sc, pf, c, key0, qpos0, S, li, g);
       else
@@ -897,9 +909,9 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       auto copies_ahead = [&](int jj) __attribute__((always_inline)) {
         if (jj + AH < n_int) {
           const int sl = (jj + AH) % R;
-          copy_group<D>(cp.k_off, kh, (pb + jj + AH) * INTERVAL_KEYS, S,
+          copy_group<D>(cp.k_off, kh, pos(jj + AH) * INTERVAL_KEYS, S,
                         kring + sl * G::SLOT_HALVES, wave);
-          copy_group<D>(cp.v_off, vh, (pb + jj + AH) * INTERVAL_KEYS, S,
+          copy_group<D>(cp.v_off, vh, pos(jj + AH) * INTERVAL_KEYS, S,
                         vring + sl * G::SLOT_HALVES, wave);
         }
       };
@@ -923,7 +935,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
         constexpr int QS = decltype(qs_flag)::value;
         constexpr int NS = decltype(nside)::value;
         constexpr int NR = decltype(nread)::value;
-        const int key0 = (pb + jj) * INTERVAL_KEYS + phase * G::BN;
+        const int key0 = pos(jj) * INTERVAL_KEYS + phase * G::BN;
         if constexpr (decltype(edge_flag)::value)
           softmax_any<D, VAR, CAUSAL, QS, QS + 1, NS, NR>(cr, sc, pf, c, key0, qpos0, S, li, g,
                                                           side);

@@ -33,3 +33,20 @@ def test_large_workload_every_head_and_row(name):
           flush=True)
     stats = compare(o, l, O, L, name)
     print(f"[gpu-parity-full] {name}: {stats}", flush=True)
+
+
+@pytest.mark.parametrize("B,H,S,D", [(1, 64, 1024, 64), (1, 64, 1024, 128), (1, 64, 1000, 64)],
+                         ids=["H64S1024D64", "H64S1024D128", "H64S1000D64"])
+def test_non_causal_rounds_every_head_and_row(B, H, S, D):
+    """512 workgroups, two rounds per XCD: with whole key intervals the second
+    round folds the keys backwards (S = 1024), with a key tail it keeps the
+    ascending order (S = 1000); both against the oracle over the whole output."""
+    from testkit import make_qkv
+
+    print(f"[gpu-parity-full] B{B} H{H} S{S} D{D} non-causal", flush=True)
+    q, k, v = make_qkv(B, H, S, D, 9700 + D + S)
+    scale = D ** -0.5
+    o, l = run_gpu(q, k, v, scale, False)
+    O, L = oracle_full(q, k, v, scale, False, workers=WORKERS)
+    stats = compare(o, l, O, L, f"B{B}H{H}S{S}D{D}")
+    print(f"[gpu-parity-full] B{B} H{H} S{S} D{D}: {stats}", flush=True)
