@@ -86,6 +86,7 @@ enum : int {
   VAR_EXP_POLY = 2,  // one exponential in four by an FMA polynomial
   VAR_WIDE = 4,      // D = 64: 64-row waves over four 32-key tiles per interval
   VAR_SUBPIPE = 8,   // D = 64: MFMAs of one sub-tile beside the softmax of the other
+  VAR_SYNC = 16,     // every K/V copy waited for and barriered right after its issue
 };
 
 template <int D, int VAR = 0>
@@ -122,7 +123,12 @@ struct Geometry {
   // (5% on causal B2 H16 S8192), not at D = 64 (5% slower, and no faster
   // with fp32-add row sums in place of the v_dot2 sums that wait for the
   // other wave's MFMAs).
-  static constexpr bool PINGPONG = D == 128;
+  static constexpr bool PINGPONG = D == 128 && (VAR & VAR_SYNC) == 0;
+  // Synchronous copies (VAR_SYNC, a check of the ring protocol): each wave
+  // waits for its copies and meets the others at a barrier right after
+  // issuing them, in lock-step order. The arithmetic is the default's, so
+  // any difference in the results would expose a race on the LDS ring.
+  static constexpr bool SYNC = (VAR & VAR_SYNC) != 0;
   // At D = 64 a tile's P.V runs in the same interval as its Q.K^T and
   // softmax (three phases, V copied one interval earlier): the SIMD's two
   // waves then interleave shorter MFMA phases with their softmaxes (1-3%
@@ -872,6 +878,10 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       if (j < n_int)
         copy_group<D>(cp.v_off, vh, pos(j) * INTERVAL_KEYS, S,
                       vring + (j & 1) * G::SLOT_HALVES, wave);
+      if constexpr (G::SYNC) {
+        wait_copies();
+        __syncthreads();
+      }
     };
     // softmax of this wave's tile of interval p (masks possible when EDGE)
     auto softmax_int = [&](int p, auto edge_flag) __attribute__((always_inline)) {
@@ -913,6 +923,10 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
                         kring + sl * G::SLOT_HALVES, wave);
           copy_group<D>(cp.v_off, vh, pos(jj + AH) * INTERVAL_KEYS, S,
                         vring + sl * G::SLOT_HALVES, wave);
+        }
+        if constexpr (G::SYNC) {
+          wait_copies();
+          __syncthreads();
         }
       };
       // End of interval jj: the copies of interval jj + 1 must have landed

@@ -123,6 +123,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
 #define ATTN_VARIANT_WIDE 4      /* D = 64: 64-row waves over four 32-key tiles  */
 #define ATTN_VARIANT_SUBPIPE 8   /* D = 64: the two 16-row sub-tiles of a wave   */
                                  /* pipelined against each other in one interval */
+#define ATTN_VARIANT_SYNC 16     /* every K/V copy waited for and barriered      */
+                                 /* right after its issue (ring-protocol check)  */
 
 /*
  * attn_fwd_variant -- attn_fwd with a chosen compiled variant of the kernel,
@@ -141,10 +143,17 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *    the other sub-tile, so the matrix and vector units of one wave overlap
  *    (Part 2, Relationship to FA-3 and FA-4: overlapping the softmax with
  *    the matrix products).
+ *  - ATTN_VARIANT_SYNC: a check of the K/V ring protocol rather than an
+ *    optimisation: every copy into LDS is waited for and followed by a
+ *    workgroup barrier right after it is issued (and D = 128 runs lock-step,
+ *    not ping-pong). Its arithmetic is the default kernel's, so its results
+ *    equal attn_fwd's bit for bit unless the default kernel reads a ring slot
+ *    before its copy lands or overwrites one still being read.
  *
  *  q ... causal, stream : as attn_fwd (same layouts, checks and status codes).
  *  variant : one of the ATTN_VARIANT_* values; D = 64 builds 0, RING3,
- *            EXP_POLY, WIDE and SUBPIPE, D = 128 builds 0 and EXP_POLY. Any other
+ *            EXP_POLY, WIDE, SUBPIPE and SYNC, D = 128 builds 0, EXP_POLY
+ *            and SYNC. Any other
  *            value (or combination) returns ATTN_ERR_UNSUPPORTED before
  *            anything is enqueued.
  */

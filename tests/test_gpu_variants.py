@@ -1,7 +1,7 @@
 """GPU parity of every compiled kernel variant (attn_fwd_variant) against the
 fp64 oracle, element by element over the whole output: the three-slot K/V
-ring and the 64-row waves at D = 64, and the exponential offload at both head
-dimensions. Shapes span several tiles with ragged tails, both masks, B > 1,
+ring, the 64-row waves and the sub-tile pipelined interval at D = 64, the
+exponential offload and the synchronous-copy check at both head dimensions. Shapes span several tiles with ragged tails, both masks, B > 1,
 negative and large scales, and rows whose running max moves mid-sequence."""
 import math
 
@@ -16,8 +16,8 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 # (D, variant) pairs built into the library, besides the default kernel
-BUILT = [(64, 1), (64, 2), (64, 4), (64, 8), (128, 2)]
-NAMES = {1: "ring3", 2: "exp_poly", 4: "wide", 8: "subpipe"}
+BUILT = [(64, 1), (64, 2), (64, 4), (64, 8), (64, 16), (128, 2), (128, 16)]
+NAMES = {1: "ring3", 2: "exp_poly", 4: "wide", 8: "subpipe", 16: "sync"}
 
 SHAPES = [
     # B, H, S, causal, scale, seed
@@ -105,3 +105,34 @@ def test_unbuilt_variant_is_refused():
     q = torch.zeros((1, 1, 64, 128), dtype=torch.float16, device="cuda:0")
     with pytest.raises(attn.AttnError, match="ATTN_ERR_UNSUPPORTED"):
         attn.fwd(q, q, q, variant=1)
+
+
+SYNC_SHAPES = [
+    # B, H, S, D, causal: tails, both masks, folded causal pairs (256 workgroups
+    # after folding), two rounds per XCD with the backwards key order
+    (2, 3, 300, 64, True),
+    (1, 2, 1000, 64, False),
+    (1, 16, 4096, 64, True),
+    (1, 64, 1024, 64, False),
+    (2, 3, 300, 128, True),
+    (1, 2, 1000, 128, False),
+    (1, 16, 4096, 128, True),
+    (1, 64, 1024, 128, False),
+]
+
+
+@pytest.mark.parametrize("shape", SYNC_SHAPES, ids=lambda c: "B{}H{}S{}D{}{}".format(
+    c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
+def test_synchronous_copies_equal_the_default_bitwise(shape):
+    """The ring-protocol check: with every copy waited for and barriered right
+    after its issue (and D = 128 in lock-step), the results must equal the
+    default kernel's bit for bit; a read of a ring slot before its copy lands,
+    or a copy over a slot still being read, would show here."""
+    B, H, S, D, causal = shape
+    print(f"[gpu-variants] sync vs default {shape}", flush=True)
+    q, k, v = make_qkv(B, H, S, D, 9800 + S + D)
+    scale = D ** -0.5
+    o0, l0 = run_variant(q, k, v, scale, causal, 0)
+    o1, l1 = run_variant(q, k, v, scale, causal, 16)
+    assert np.array_equal(o0.view(np.uint16), o1.view(np.uint16)), f"{shape}: O differs"
+    assert np.array_equal(l0.view(np.uint32), l1.view(np.uint32)), f"{shape}: LSE differs"
