@@ -87,6 +87,7 @@ enum : int {
   VAR_WIDE = 4,      // D = 64: 64-row waves over four 32-key tiles per interval
   VAR_SUBPIPE = 8,   // D = 64: MFMAs of one sub-tile beside the softmax of the other
   VAR_SYNC = 16,     // every K/V copy waited for and barriered right after its issue
+  VAR_BAR2 = 32,     // D = 64: one workgroup barrier per two key intervals (four-slot ring)
 };
 
 template <int D, int VAR = 0>
@@ -112,7 +113,13 @@ struct Geometry {
   // group is read while the next is copied. A three-slot ring (VAR_RING3,
   // D = 64 only: at D = 128 it does not fit next to the Q tile) runs the
   // copies two intervals ahead; it measured no faster.
-  static constexpr int RING = (D == 64 && (VAR & VAR_RING3) != 0) ? 3 : 2;
+  // One barrier per two intervals (VAR_BAR2, D = 64): a four-slot ring with
+  // the copies two intervals ahead, so that every slot written after a
+  // barrier was last read before it, and every slot read before the next
+  // barrier was waited for at this one.
+  static constexpr bool BAR2 = D == 64 && (VAR & VAR_BAR2) != 0;
+  static constexpr int RING = BAR2 ? 4 : (D == 64 && (VAR & VAR_RING3) != 0) ? 3 : 2;
+  static constexpr int AHEAD = BAR2 ? 2 : RING - 1;  // intervals between a copy and its use
   static constexpr int SLOT_HALVES = NPH * K_HALVES;        // one interval's tiles
   // At D = 128 the Q fragments would not fit the register budget next to the
   // output accumulators: the workgroup's Q rows are staged in LDS instead.
@@ -847,7 +854,14 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     if constexpr (G::PV_SAME) {
       if (n_int > 0) copy_group<D>(cp.v_off, vh, pos(0) * INTERVAL_KEYS, S, vring, wave);  // V of step 0
     }
-    if constexpr (G::PV_SAME && R == 3) {
+    if constexpr (G::PV_SAME && G::BAR2) {
+      // four-slot ring: steps 0 and 1 land before the first barrier
+      if (n_int > 1) {
+        copy_group<D>(cp.k_off, kh, pos(1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, wave);
+        copy_group<D>(cp.v_off, vh, pos(1) * INTERVAL_KEYS, S, vring + G::SLOT_HALVES, wave);
+      }
+      wait_copies();
+    } else if constexpr (G::PV_SAME && R == 3) {
       // three-slot ring: step 1 is in flight from the start
       if (n_int > 1) {
         copy_group<D>(cp.k_off, kh, pos(1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, wave);
@@ -915,7 +929,7 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       // runs n_int intervals. With a three-slot ring the copies run two
       // intervals ahead of their use, so their latency (about as long as an
       // interval) is off the barrier's critical path.
-      constexpr int AH = R - 1;  // intervals between a copy and its use
+      constexpr int AH = G::AHEAD;  // intervals between a copy and its use
       auto copies_ahead = [&](int jj) __attribute__((always_inline)) {
         if (jj + AH < n_int) {
           const int sl = (jj + AH) % R;
@@ -933,6 +947,15 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       // (those of jj + 2, issued in this interval, may still run).
       auto end_int = [&](int jj) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (G::BAR2) {
+          // barrier after odd steps only: copies issued in steps jj - 1 and jj
+          // (for jj + 1 and jj + 2, both read before the next barrier) land
+          if (jj & 1) {
+            wait_copies();
+            __syncthreads();
+          }
+          return;
+        }
         if (R > 2 && jj + AH < n_int)
           wait_copies_keep<2 * G::LOADS>();
         else
@@ -1010,11 +1033,20 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       using S0 = std::integral_constant<int, 0>;
       using S1 = std::integral_constant<int, 1>;
       using S2 = std::integral_constant<int, 2>;
+      using S3 = std::integral_constant<int, 3>;
       using SR = std::integral_constant<int, -1>;
       // Steady state unrolled by the ring depth, so that the ring slots are
       // constant offsets of the LDS reads rather than addresses computed per
       // interval.
-      if constexpr (R == 3) {
+      if constexpr (R == 4) {
+        for (; j + 4 < n_live; j += 4) {
+          full(j, F_{}, S0{});
+          full(j + 1, F_{}, S1{});
+          full(j + 2, F_{}, S2{});
+          full(j + 3, F_{}, S3{});
+        }
+        for (; j + 1 < n_live; ++j) full(j, F_{}, SR{});
+      } else if constexpr (R == 3) {
         for (; j + 3 < n_live; j += 3) {
           full(j, F_{}, S0{});
           full(j + 1, F_{}, S1{});
@@ -1032,6 +1064,13 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       for (; j < n_int; ++j) {
         copies_ahead(j);
         end_int(j);
+      }
+      if constexpr (G::BAR2) {
+        // the last step was even: no barrier ended it
+        if (n_int > 0 && ((n_int - 1) & 1) == 0) {
+          wait_copies();
+          __syncthreads();
+        }
       }
     } else {
       // Two-phase order as one instruction stream for every wave: interval

@@ -125,6 +125,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                                  /* pipelined against each other in one interval */
 #define ATTN_VARIANT_SYNC 16     /* every K/V copy waited for and barriered      */
                                  /* right after its issue (ring-protocol check)  */
+#define ATTN_VARIANT_BAR2 32     /* D = 64: one workgroup barrier per two key    */
+                                 /* intervals, four-slot K/V ring                */
 
 /*
  * attn_fwd_variant -- attn_fwd with a chosen compiled variant of the kernel,
@@ -143,6 +145,10 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *    the other sub-tile, so the matrix and vector units of one wave overlap
  *    (Part 2, Relationship to FA-3 and FA-4: overlapping the softmax with
  *    the matrix products).
+ *  - ATTN_VARIANT_BAR2: one workgroup barrier per two key intervals instead
+ *    of one per interval, with a four-slot K/V ring and the copies two
+ *    intervals ahead (Part 2, Refused Optimizations: deeper rings; fewer
+ *    barriers let the two waves of a SIMD drift apart).
  *  - ATTN_VARIANT_SYNC: a check of the K/V ring protocol rather than an
  *    optimisation: every copy into LDS is waited for and followed by a
  *    workgroup barrier right after it is issued (and D = 128 runs lock-step,
@@ -152,8 +158,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *
  *  q ... causal, stream : as attn_fwd (same layouts, checks and status codes).
  *  variant : one of the ATTN_VARIANT_* values; D = 64 builds 0, RING3,
- *            EXP_POLY, WIDE, SUBPIPE and SYNC, D = 128 builds 0, EXP_POLY
- *            and SYNC. Any other
+ *            EXP_POLY, WIDE, SUBPIPE, SYNC and BAR2, D = 128 builds 0,
+ *            EXP_POLY and SYNC. Any other
  *            value (or combination) returns ATTN_ERR_UNSUPPORTED before
  *            anything is enqueued.
  */
