@@ -127,9 +127,9 @@ struct Geometry {
   // The second wave of each SIMD (waves 4-7) runs half an interval out of
   // phase with the first (softmax against the other wave's MFMA phase). This
   // pays only where the MFMA phase is long next to the softmax: at D = 128
-  // (5% on causal B2 H16 S8192), not at D = 64 (5% slower, and no faster
-  // with fp32-add row sums in place of the v_dot2 sums that wait for the
-  // other wave's MFMAs).
+  // (5% on causal B2 H16 S8192), not at D = 64 (2-10% slower, 3-4% with
+  // fp32-add row sums in place of the v_dot2 sums that wait for the other
+  // wave's MFMAs, and no better with the V operands in registers).
   static constexpr bool PINGPONG = D == 128 && (VAR & VAR_SYNC) == 0;
   // Synchronous copies (VAR_SYNC, a check of the ring protocol): each wave
   // waits for its copies and meets the others at a barrier right after
