@@ -580,7 +580,7 @@ template <int D, int VAR, bool CAUSAL, bool MASK, int QS_LO = 0, int QS_HI = -1,
 __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
                                              const ScoreSet<D, VAR>& sc,
                                              ProbSet<D, VAR>& pf, float c, int key0,
-                                             int qpos0, int S, int li, int g,
+                                             int qpos0, int S, int li, int g, bool first,
                                              Side&& side = Side{}) {
   using G = Geometry<D, VAR>;
   constexpr int QSUB = QS_HI < 0 ? G::QSUB : QS_HI;  // one past the last sub-tile
@@ -638,8 +638,14 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
     else
       tsum[qs] = acc[0] + acc[1];
   };
+  // The first step of a tile starts from m = -inf, so its probabilities
+  // overflow by construction: there the row max is taken first and the
+  // exponentials are computed once, against it (the same arithmetic as the
+  // redo below, without the wasted first pass).
+  if (!first) {
 #pragma unroll
-  for (int qs = QS_LO; qs < QSUB; ++qs) expo(qs);
+    for (int qs = QS_LO; qs < QSUB; ++qs) expo(qs);
+  }
   if constexpr (SIDE_MFMAS > 0) {
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, SIDE_READS, 0);
     pin_side_mfmas<G::SIDE_VPER, 0, SIDE_MFMAS>();
@@ -651,13 +657,15 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
   auto big = [&](int qs) {
     return SUM_ONTO_D ? !(dnew[qs] <= cr[qs].d + P_LIMIT) : !(tsum[qs] <= P_LIMIT);
   };
-  bool over = false;
+  bool over = first;
+  if (!first) {
 #pragma unroll
-  for (int qs = QS_LO; qs < QSUB; ++qs) over = over || big(qs);
+    for (int qs = QS_LO; qs < QSUB; ++qs) over = over || big(qs);
+  }
   if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
     for (int qs = QS_LO; qs < QSUB; ++qs) {
-      if (__builtin_amdgcn_ballot_w64(big(qs)) == 0) continue;
+      if (!first && __builtin_amdgcn_ballot_w64(big(qs)) == 0) continue;
       float tmax = NEG_BIG;
 #pragma unroll
       for (int kb = 0; kb < G::KB; ++kb) {
@@ -687,7 +695,7 @@ template <int D, int VAR, bool CAUSAL, int QS_LO = 0, int QS_HI = -1, int SIDE_M
 __device__ __forceinline__ void softmax_any(CarrierSet<D, VAR>& cr,
                                             const ScoreSet<D, VAR>& sc,
                                             ProbSet<D, VAR>& pf, float c, int key0,
-                                            int qpos0, int S, int li, int g,
+                                            int qpos0, int S, int li, int g, bool first,
                                             Side&& side = Side{}) {
   constexpr int BN = Geometry<D, VAR>::BN;
   // Element masks are needed on the sequence tail and on tiles reaching past
@@ -695,10 +703,10 @@ __device__ __forceinline__ void softmax_any(CarrierSet<D, VAR>& cr,
   const bool needs_mask = (key0 + BN > S) || (CAUSAL && key0 + BN - 1 > qpos0);
   if (needs_mask)
     softmax_tile<D, VAR, CAUSAL, true, QS_LO, QS_HI, SIDE_MFMAS, SIDE_READS>(
-        cr, sc, pf, c, key0, qpos0, S, li, g, side);
+        cr, sc, pf, c, key0, qpos0, S, li, g, first, side);
   else
     softmax_tile<D, VAR, CAUSAL, false, QS_LO, QS_HI, SIDE_MFMAS, SIDE_READS>(
-        cr, sc, pf, c, key0, qpos0, S, li, g, side);
+        cr, sc, pf, c, key0, qpos0, S, li, g, first, side);
 }
 
 // Workgroup id -> (batch*head, query tiles) by `order` (work_order.h).
@@ -902,9 +910,9 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(2);
       const int key0 = pos(p) * INTERVAL_KEYS + phase * G::BN;
       if constexpr (decltype(edge_flag)::value)
-        softmax_any<D, VAR, CAUSAL>(cr, sc, pf, c, key0, qpos0, S, li, g);
+        softmax_any<D, VAR, CAUSAL>(cr, sc, pf, c, key0, qpos0, S, li, g, p == 0);
       else
-        softmax_tile<D, VAR, CAUSAL, false>(cr, sc, pf, c, key0, qpos0, S, li, g);
+        softmax_tile<D, VAR, CAUSAL, false>(cr, sc, pf, c, key0, qpos0, S, li, g, p == 0);
       if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(0);
     };
     auto mfma = [&](int j, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
@@ -975,10 +983,10 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
         const int key0 = pos(jj) * INTERVAL_KEYS + phase * G::BN;
         if constexpr (decltype(edge_flag)::value)
           softmax_any<D, VAR, CAUSAL, QS, QS + 1, NS, NR>(cr, sc, pf, c, key0, qpos0, S, li, g,
-                                                          side);
+                                                          jj == 0, side);
         else
           softmax_tile<D, VAR, CAUSAL, false, QS, QS + 1, NS, NR>(cr, sc, pf, c, key0, qpos0, S,
-                                                                  li, g, side);
+                                                                  li, g, jj == 0, side);
       };
       auto full_sp = [&](int jj, auto edge_flag, auto slot_flag) __attribute__((always_inline)) {
         if constexpr (G::SUBPIPE) {
