@@ -18,7 +18,8 @@ static_assert(attn::COMBINE_THREADS == attn::plan::COMBINE_THREADS, "combine wor
 static_assert(attn::MAX_SPLITS == ATTN_MAX_SPLITS, "split limit of the kernel and of the header");
 static_assert(attn::VAR_RING3 == ATTN_VARIANT_RING3 && attn::VAR_EXP_POLY == ATTN_VARIANT_EXP_POLY &&
                   attn::VAR_WIDE == ATTN_VARIANT_WIDE && attn::VAR_SUBPIPE == ATTN_VARIANT_SUBPIPE &&
-                  attn::VAR_SYNC == ATTN_VARIANT_SYNC && attn::VAR_BAR2 == ATTN_VARIANT_BAR2,
+                  attn::VAR_SYNC == ATTN_VARIANT_SYNC && attn::VAR_BAR2 == ATTN_VARIANT_BAR2 &&
+                  attn::VAR_PROD == ATTN_VARIANT_PROD,
               "variant flags of the kernel and of the header");
 
 namespace {
@@ -44,9 +45,13 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   const _Float16* kh = static_cast<const _Float16*>(k);
   const _Float16* vh = static_cast<const _Float16*>(v);
   _Float16* oh = static_cast<_Float16*>(o);
+  constexpr int WG_THREADS = Geometry<D, VAR>::WG_THREADS;  // 512, or 768 with producer waves
+  if (L.blocks * WG_THREADS > plan::MAX_WORK_ITEMS)
+    return plan::fail(msg(), ATTN_ERR_SHAPE, "grid of %lld workgroups x %d threads exceeds 2^32 work-items",
+                      (long long)L.blocks, WG_THREADS);
   if (n_splits == 1) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, VAR>), dim3((unsigned)L.blocks),
-                       dim3(THREADS), 0, stream, qh, kh, vh, oh, lse, BH, Sq, Sk, L.n_qtiles, 1,
+                       dim3(WG_THREADS), 0, stream, qh, kh, vh, oh, lse, BH, Sq, Sk, L.n_qtiles, 1,
                        L.order, c, qsign, nullptr, nullptr);
   } else if constexpr (VAR == 0) {
     float* part_o = static_cast<float*>(workspace);
@@ -107,6 +112,7 @@ int dispatch_variant(const void* q, const void* k, const void* v, void* o, float
       case VAR_SUBPIPE: return launch_variant<64, VAR_SUBPIPE>(q, k, v, o, lse, B, H, S, scale, causal, st);
       case VAR_SYNC: return launch_variant<64, VAR_SYNC>(q, k, v, o, lse, B, H, S, scale, causal, st);
       case VAR_BAR2: return launch_variant<64, VAR_BAR2>(q, k, v, o, lse, B, H, S, scale, causal, st);
+      case VAR_PROD: return launch_variant<64, VAR_PROD>(q, k, v, o, lse, B, H, S, scale, causal, st);
       default: break;
     }
   } else {
@@ -118,10 +124,11 @@ int dispatch_variant(const void* q, const void* k, const void* v, void* o, float
     }
   }
   return attn::plan::fail(msg(), ATTN_ERR_UNSUPPORTED,
-                          "kernel variant %d is not built for D=%d (D=64: 0, %d, %d, %d, %d, %d, %d; "
+                          "kernel variant %d is not built for D=%d (D=64: 0, %d, %d, %d, %d, %d, %d, %d; "
                           "D=128: 0, %d, %d)", variant, D, ATTN_VARIANT_RING3, ATTN_VARIANT_EXP_POLY,
                           ATTN_VARIANT_WIDE, ATTN_VARIANT_SUBPIPE, ATTN_VARIANT_SYNC,
-                          ATTN_VARIANT_BAR2, ATTN_VARIANT_EXP_POLY, ATTN_VARIANT_SYNC);
+                          ATTN_VARIANT_BAR2, ATTN_VARIANT_PROD, ATTN_VARIANT_EXP_POLY,
+                          ATTN_VARIANT_SYNC);
 }
 
 // Checks shared by the entry points (Sq query rows against Sk keys).

@@ -88,6 +88,7 @@ enum : int {
   VAR_SUBPIPE = 8,   // D = 64: MFMAs of one sub-tile beside the softmax of the other
   VAR_SYNC = 16,     // every K/V copy waited for and barriered right after its issue
   VAR_BAR2 = 32,     // D = 64: one workgroup barrier per two key intervals (four-slot ring)
+  VAR_PROD = 64,     // D = 64: four producer waves issue every K/V copy
 };
 
 template <int D, int VAR = 0>
@@ -158,11 +159,21 @@ struct Geometry {
   static constexpr int Q_HALVES = Q_IN_LDS ? BLOCK_M * D : 0;
   static constexpr int D_CHUNKS = D / 32;                  // contraction chunks of Q.K
   static constexpr int D_BLOCKS = D / 16;                  // 16-row blocks of O^T
+  // Producer waves (VAR_PROD, D = 64): the workgroup gets four more waves,
+  // one per SIMD, that issue all K/V copies and only wait and synchronise;
+  // the eight compute waves never touch global memory inside the key loop.
+  // At 159 VGPRs three waves fit a SIMD's 512 registers per lane.
+  static constexpr bool PROD = D == 64 && PV_SAME && (VAR & VAR_PROD) != 0;
+  static constexpr int PRODUCERS = PROD ? 4 : 0;
+  static constexpr int WG_WAVES = WAVES + PRODUCERS;
+  static constexpr int WG_THREADS = 64 * WG_WAVES;
+  static constexpr int NCOP = PROD ? PRODUCERS : WAVES;  // waves that issue the copies
   // per interval, K and V each in 16-byte pieces
   static constexpr int PIECES = NPH * BN * (D / 8);
-  static constexpr int LOADS = PIECES / THREADS;
+  static constexpr int LOADS = PIECES / (64 * NCOP);   // copies per copying wave and tensor
   static_assert(D % 64 == 0, "D must be a multiple of 64");
-  static_assert(LOADS * THREADS == PIECES, "tiling");
+  static_assert(LOADS * 64 * NCOP == PIECES, "tiling");
+  static_assert(!PROD || VAR == VAR_PROD, "producer waves run the default two-slot ring alone");
   static_assert(QSUB * 16 * QGROUPS == BLOCK_M && KB >= 2 && KC >= 1, "geometry");
   // Carrier hand-off (after the key loop): each wave finalises OWN_DB of the
   // output's 16-column blocks for its rows. Per wave, 16-byte slots of 64
@@ -237,25 +248,26 @@ __device__ __forceinline__ int v_swizzle(int r) {
 // 1 KB of LDS in slot order; each lane therefore fetches the global piece that
 // belongs in its slot. Per-lane byte offsets (relative to the first key of the
 // interval) are precomputed for K and for V.
-template <int D>
+template <int D, int VAR>
 struct CopyPlan {
-  uint32_t k_off[Geometry<D>::LOADS];
-  uint32_t v_off[Geometry<D>::LOADS];
+  uint32_t k_off[Geometry<D, VAR>::LOADS];
+  uint32_t v_off[Geometry<D, VAR>::LOADS];
 };
 
-template <int D>
-__device__ __forceinline__ int copy_unit(int wave, int i) {
-  return i * WAVES + wave;  // 1 KB unit of the slot filled by instruction i of a wave
+// 1 KB unit of the slot filled by instruction i of copying wave cw
+template <int D, int VAR>
+__device__ __forceinline__ int copy_unit(int cw, int i) {
+  return i * Geometry<D, VAR>::NCOP + cw;
 }
 
-template <int D>
-__device__ __forceinline__ void make_copy_plan(CopyPlan<D>& cp, int wave, int lane) {
-  using G = Geometry<D>;
+template <int D, int VAR>
+__device__ __forceinline__ void make_copy_plan(CopyPlan<D, VAR>& cp, int cw, int lane) {
+  using G = Geometry<D, VAR>;
   constexpr int CHUNKS = D / 8;                     // 16-byte chunks per row
   constexpr int TILE_SLOTS = G::BN * CHUNKS;
 #pragma unroll
-  for (int i = 0; i < Geometry<D>::LOADS; ++i) {
-    const int slot = copy_unit<D>(wave, i) * 64 + lane;
+  for (int i = 0; i < G::LOADS; ++i) {
+    const int slot = copy_unit<D, VAR>(cw, i) * 64 + lane;
     const int t = slot / TILE_SLOTS;                // tile of the interval
     const int w = slot % TILE_SLOTS;
     const int row = w / CHUNKS;
@@ -276,13 +288,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t keys_from(const _Float16* base
 
 // Issue the direct copy of the interval starting at key0 into `slot` (its LDS
 // area: tile 0, tile 1, ...). Completion is awaited with vmcnt.
-template <int D>
+template <int D, int VAR>
 __device__ __forceinline__ void copy_group(const uint32_t* off, const _Float16* base, int key0,
-                                          int S, _Float16* slot, int wave) {
+                                          int S, _Float16* slot, int cw) {
   const __amdgpu_buffer_rsrc_t rs = keys_from<D>(base, key0, S);
 #pragma unroll
-  for (int i = 0; i < Geometry<D>::LOADS; ++i) {
-    _Float16* dst = slot + copy_unit<D>(wave, i) * 64 * 8;   // 64 slots of 8 halves
+  for (int i = 0; i < Geometry<D, VAR>::LOADS; ++i) {
+    _Float16* dst = slot + copy_unit<D, VAR>(cw, i) * 64 * 8;   // 64 slots of 8 halves
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (__attribute__((address_space(3))) void*)dst, 16, off[i], 0, 0, 0);
   }
@@ -726,7 +738,7 @@ __device__ __forceinline__ void softmax_any(CarrierSet<D, VAR>& cr,
 // stores the partial result -- o/d in fp32 and m + log2(d) -- into the
 // workspace instead of O and LSE; attn_combine_kernel merges the runs.
 template <int D, bool CAUSAL, bool SPLIT, int VAR = 0>
-__global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
+__global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
     int BH, int Sq, int Sk, int n_qtiles, int n_splits, int order, float c, uint32_t qsign,
@@ -771,6 +783,10 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     const int qgrp = wave / NPH;
     const int phase = wave % NPH;
     const bool late = wave >= WAVES / 2;  // second wave of its SIMD
+    // With producer waves (waves 8-11) the copies are theirs alone; else
+    // every wave copies its share.
+    const bool producer = G::PROD && wave >= WAVES;
+    const int cw = G::PROD ? wave - WAVES : wave;  // index among the copying waves
     const int q0 = qt * BLOCK_M;
     const int qrow0 = q0 + G::ROWS * qgrp;  // this wave's first query row
     const int qpos0 = qrow0 + koff;         // its sequence position
@@ -779,7 +795,9 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     // into registers, or (Q_IN_LDS) the workgroup's Q rows into LDS by direct
     // copies, chunks permuted like K rows; rows past S read as zeros.
     f16x8 qf[QSUB][G::D_CHUNKS];
-    if constexpr (G::Q_IN_LDS) {
+    if (producer) {
+      // no query rows
+    } else if constexpr (G::Q_IN_LDS) {
       constexpr int UNITS = BLOCK_M * D * 2 / 1024;  // 1 KB copy units
       static_assert(UNITS % WAVES == 0, "Q copy split");
   #pragma unroll
@@ -856,24 +874,27 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
                            ((blockIdx.x >> 8) & 1u) != 0u;
     auto pos = [&](int x) { return pb + (backwards ? n_int - 1 - x : x); };
 
-    CopyPlan<D> cp;
-    make_copy_plan<D>(cp, wave, lane);
-    if (n_int > 0) copy_group<D>(cp.k_off, kh, pos(0) * INTERVAL_KEYS, S, kring, wave);  // K of step 0
+    CopyPlan<D, VAR> cp;
+    make_copy_plan<D, VAR>(cp, cw, lane);
+    const bool copier = !G::PROD || producer;
+    if (copier && n_int > 0)
+      copy_group<D, VAR>(cp.k_off, kh, pos(0) * INTERVAL_KEYS, S, kring, cw);  // K of step 0
     if constexpr (G::PV_SAME) {
-      if (n_int > 0) copy_group<D>(cp.v_off, vh, pos(0) * INTERVAL_KEYS, S, vring, wave);  // V of step 0
+      if (copier && n_int > 0)
+        copy_group<D, VAR>(cp.v_off, vh, pos(0) * INTERVAL_KEYS, S, vring, cw);  // V of step 0
     }
     if constexpr (G::PV_SAME && G::BAR2) {
       // four-slot ring: steps 0 and 1 land before the first barrier
       if (n_int > 1) {
-        copy_group<D>(cp.k_off, kh, pos(1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, wave);
-        copy_group<D>(cp.v_off, vh, pos(1) * INTERVAL_KEYS, S, vring + G::SLOT_HALVES, wave);
+        copy_group<D, VAR>(cp.k_off, kh, pos(1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, cw);
+        copy_group<D, VAR>(cp.v_off, vh, pos(1) * INTERVAL_KEYS, S, vring + G::SLOT_HALVES, cw);
       }
       wait_copies();
     } else if constexpr (G::PV_SAME && R == 3) {
       // three-slot ring: step 1 is in flight from the start
       if (n_int > 1) {
-        copy_group<D>(cp.k_off, kh, pos(1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, wave);
-        copy_group<D>(cp.v_off, vh, pos(1) * INTERVAL_KEYS, S, vring + G::SLOT_HALVES, wave);
+        copy_group<D, VAR>(cp.k_off, kh, pos(1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, cw);
+        copy_group<D, VAR>(cp.v_off, vh, pos(1) * INTERVAL_KEYS, S, vring + G::SLOT_HALVES, cw);
         wait_copies_keep<2 * G::LOADS>();
       } else {
         wait_copies();
@@ -882,6 +903,28 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       wait_copies();
     }
     __syncthreads();
+
+    if constexpr (G::PROD) {
+      if (producer) {
+        // Interval j: right after the barrier that ends interval j - 1 (whose
+        // slot the compute waves no longer read), copy K and V of interval
+        // j + 1 into that slot; wait; meet the compute waves at the barrier
+        // that ends interval j. Then the epilogue's barrier, and done.
+        for (int j = 0; j < n_int; ++j) {
+          if (j + 1 < n_int) {
+            const int sl = (j + 1) % R;
+            copy_group<D, VAR>(cp.k_off, kh, pos(j + 1) * INTERVAL_KEYS, S,
+                               kring + sl * G::SLOT_HALVES, cw);
+            copy_group<D, VAR>(cp.v_off, vh, pos(j + 1) * INTERVAL_KEYS, S,
+                               vring + sl * G::SLOT_HALVES, cw);
+          }
+          wait_copies();
+          __syncthreads();
+        }
+        __syncthreads();  // the carrier hand-off of the compute waves
+        return;
+      }
+    }
 
     // Two-phase order (D = 128), barrier interval j (counted from pb): P.V of
     // interval j-1 and Q.K^T of interval j (MFMA), then the copies of K of
@@ -895,11 +938,11 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
     // branches.
     auto copies = [&](int j) __attribute__((always_inline)) {
       if (j + 1 < n_int)
-        copy_group<D>(cp.k_off, kh, pos(j + 1) * INTERVAL_KEYS, S,
-                      kring + ((j + 1) & 1) * G::SLOT_HALVES, wave);
+        copy_group<D, VAR>(cp.k_off, kh, pos(j + 1) * INTERVAL_KEYS, S,
+                      kring + ((j + 1) & 1) * G::SLOT_HALVES, cw);
       if (j < n_int)
-        copy_group<D>(cp.v_off, vh, pos(j) * INTERVAL_KEYS, S,
-                      vring + (j & 1) * G::SLOT_HALVES, wave);
+        copy_group<D, VAR>(cp.v_off, vh, pos(j) * INTERVAL_KEYS, S,
+                      vring + (j & 1) * G::SLOT_HALVES, cw);
       if constexpr (G::SYNC) {
         wait_copies();
         __syncthreads();
@@ -939,12 +982,12 @@ __global__ __launch_bounds__(THREADS) void attn_fwd_kernel(
       // interval) is off the barrier's critical path.
       constexpr int AH = G::AHEAD;  // intervals between a copy and its use
       auto copies_ahead = [&](int jj) __attribute__((always_inline)) {
-        if (jj + AH < n_int) {
+        if (!G::PROD && jj + AH < n_int) {
           const int sl = (jj + AH) % R;
-          copy_group<D>(cp.k_off, kh, pos(jj + AH) * INTERVAL_KEYS, S,
-                        kring + sl * G::SLOT_HALVES, wave);
-          copy_group<D>(cp.v_off, vh, pos(jj + AH) * INTERVAL_KEYS, S,
-                        vring + sl * G::SLOT_HALVES, wave);
+          copy_group<D, VAR>(cp.k_off, kh, pos(jj + AH) * INTERVAL_KEYS, S,
+                        kring + sl * G::SLOT_HALVES, cw);
+          copy_group<D, VAR>(cp.v_off, vh, pos(jj + AH) * INTERVAL_KEYS, S,
+                        vring + sl * G::SLOT_HALVES, cw);
         }
         if constexpr (G::SYNC) {
           wait_copies();

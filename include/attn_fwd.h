@@ -127,6 +127,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                                  /* right after its issue (ring-protocol check)  */
 #define ATTN_VARIANT_BAR2 32     /* D = 64: one workgroup barrier per two key    */
                                  /* intervals, four-slot K/V ring                */
+#define ATTN_VARIANT_PROD 64     /* D = 64: four producer waves issue the K/V    */
+                                 /* copies (768-thread workgroups)               */
 
 /*
  * attn_fwd_variant -- attn_fwd with a chosen compiled variant of the kernel,
@@ -149,6 +151,10 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *    of one per interval, with a four-slot K/V ring and the copies two
  *    intervals ahead (Part 2, Refused Optimizations: deeper rings; fewer
  *    barriers let the two waves of a SIMD drift apart).
+ *  - ATTN_VARIANT_PROD: four more waves per workgroup, one per SIMD, issue
+ *    every K/V copy and only wait and synchronise, so that the eight compute
+ *    waves never touch global memory inside the key loop (Part 2, Refused
+ *    Optimizations: the producer warp of warp specialisation).
  *  - ATTN_VARIANT_SYNC: a check of the K/V ring protocol rather than an
  *    optimisation: every copy into LDS is waited for and followed by a
  *    workgroup barrier right after it is issued (and D = 128 runs lock-step,
@@ -158,7 +164,7 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *
  *  q ... causal, stream : as attn_fwd (same layouts, checks and status codes).
  *  variant : one of the ATTN_VARIANT_* values; D = 64 builds 0, RING3,
- *            EXP_POLY, WIDE, SUBPIPE, SYNC and BAR2, D = 128 builds 0,
+ *            EXP_POLY, WIDE, SUBPIPE, SYNC, BAR2 and PROD, D = 128 builds 0,
  *            EXP_POLY and SYNC. Any other
  *            value (or combination) returns ATTN_ERR_UNSUPPORTED before
  *            anything is enqueued.
