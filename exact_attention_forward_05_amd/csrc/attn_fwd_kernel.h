@@ -89,6 +89,7 @@ enum : int {
   VAR_SYNC = 16,     // every K/V copy waited for and barriered right after its issue
   VAR_BAR2 = 32,     // D = 64: one workgroup barrier per two key intervals (four-slot ring)
   VAR_PROD = 64,     // D = 64: four producer waves issue every K/V copy
+  VAR_TRIO = 128,    // D = 64: three waves per SIMD over three 64-key tiles per interval
 };
 
 template <int D, int VAR = 0>
@@ -98,14 +99,20 @@ struct Geometry {
   // but measured no faster than 32-row waves (the path is not bound by
   // them), so they are a variant.
   static constexpr bool WIDE = D == 64 && (VAR & VAR_WIDE) != 0;
-  static constexpr int NPH = WIDE ? 4 : 2;
-  static constexpr int QGROUPS = WAVES / NPH;              // query groups
+  // Three waves per SIMD (VAR_TRIO, D = 64): twelve compute waves, three per
+  // query group, each on its own 64-key tile of a 192-key interval (three
+  // 159-VGPR allocations fit a SIMD's 512 registers per lane).
+  static constexpr bool TRIO = D == 64 && (VAR & VAR_TRIO) != 0;
+  static constexpr int NPH = WIDE ? 4 : TRIO ? 3 : 2;
+  static constexpr int CWAVES = TRIO ? 12 : WAVES;         // compute waves
+  static constexpr int QGROUPS = CWAVES / NPH;             // query groups
   static constexpr int ROWS = BLOCK_M / QGROUPS;           // query rows per wave
   static constexpr int QSUB = ROWS / 16;                   // 16-row query sub-tiles per wave
   // Keys per tile: each wave folds one tile per barrier interval. (At D = 64,
   // 64-row waves with 64-key tiles would not fit the 256-register budget of
   // two waves per SIMD; nor would 128-key tiles with 32-row waves.)
-  static constexpr int BN = INTERVAL_KEYS / NPH;
+  static constexpr int BN = TRIO ? 64 : INTERVAL_KEYS / NPH;
+  static constexpr int IKEYS = NPH * BN;                   // keys per barrier interval
   static constexpr int KB = BN / 16;                       // 16-key MFMA blocks of S^T
   static constexpr int KC = BN / 32;                       // 32-key chunks of the P.V contraction
   static constexpr int K_HALVES = BN * D;                  // K rows unpadded, swizzled
@@ -165,28 +172,31 @@ struct Geometry {
   // At 159 VGPRs three waves fit a SIMD's 512 registers per lane.
   static constexpr bool PROD = D == 64 && PV_SAME && (VAR & VAR_PROD) != 0;
   static constexpr int PRODUCERS = PROD ? 4 : 0;
-  static constexpr int WG_WAVES = WAVES + PRODUCERS;
+  static constexpr int WG_WAVES = CWAVES + PRODUCERS;
   static constexpr int WG_THREADS = 64 * WG_WAVES;
-  static constexpr int NCOP = PROD ? PRODUCERS : WAVES;  // waves that issue the copies
+  static constexpr int NCOP = PROD ? PRODUCERS : CWAVES;  // waves that issue the copies
   // per interval, K and V each in 16-byte pieces
   static constexpr int PIECES = NPH * BN * (D / 8);
   static constexpr int LOADS = PIECES / (64 * NCOP);   // copies per copying wave and tensor
   static_assert(D % 64 == 0, "D must be a multiple of 64");
   static_assert(LOADS * 64 * NCOP == PIECES, "tiling");
   static_assert(!PROD || VAR == VAR_PROD, "producer waves run the default two-slot ring alone");
+  static_assert(!TRIO || (VAR & ~VAR_SYNC) == VAR_TRIO,
+                "three waves per SIMD run the default order (or its synchronous-copy check)");
   static_assert(QSUB * 16 * QGROUPS == BLOCK_M && KB >= 2 && KC >= 1, "geometry");
-  // Carrier hand-off (after the key loop): each wave finalises OWN_DB of the
-  // output's 16-column blocks for its rows. Per wave, 16-byte slots of 64
-  // lanes: {m, d} of two sub-tiles per slot, then one slot per sub-tile and
-  // output block.
-  static constexpr int OWN_DB = D_BLOCKS / NPH;
+  // Carrier hand-off (after the key loop): each wave finalises the output's
+  // 16-column blocks it owns (block db belongs to phase db * NPH / D_BLOCKS:
+  // an equal share, or at NPH = 3 blocks {0, 1}, {2}, {3}) for its rows. Per
+  // wave, 16-byte slots of 64 lanes: {m, d} of two sub-tiles per slot, then
+  // one slot per sub-tile and output block.
+  static constexpr int owner(int db) { return db * NPH / D_BLOCKS; }
   static constexpr int MD_SLOTS = (QSUB + 1) / 2;
   static constexpr int HANDOFF_SLOTS = MD_SLOTS + QSUB * D_BLOCKS;
-  static constexpr int HANDOFF_BYTES = WAVES * HANDOFF_SLOTS * 64 * 16;
+  static constexpr int HANDOFF_BYTES = CWAVES * HANDOFF_SLOTS * 64 * 16;
   static constexpr int LOOP_BYTES = (2 * RING * SLOT_HALVES + Q_HALVES) * 2;
   static constexpr int LDS_BYTES = LOOP_BYTES > HANDOFF_BYTES ? LOOP_BYTES : HANDOFF_BYTES;
   static constexpr int LDS_HALVES = LDS_BYTES / 2;
-  static_assert(OWN_DB * NPH == D_BLOCKS, "output blocks split over a query group");
+  static_assert(D_BLOCKS >= NPH, "every wave of a query group owns an output block");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -785,8 +795,8 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     const bool late = wave >= WAVES / 2;  // second wave of its SIMD
     // With producer waves (waves 8-11) the copies are theirs alone; else
     // every wave copies its share.
-    const bool producer = G::PROD && wave >= WAVES;
-    const int cw = G::PROD ? wave - WAVES : wave;  // index among the copying waves
+    const bool producer = G::PROD && wave >= G::CWAVES;
+    const int cw = G::PROD ? wave - G::CWAVES : wave;  // index among the copying waves
     const int q0 = qt * BLOCK_M;
     const int qrow0 = q0 + G::ROWS * qgrp;  // this wave's first query row
     const int qpos0 = qrow0 + koff;         // its sequence position
@@ -870,7 +880,7 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     // K/V that the round before it left in the XCD's L2 (at B1 H8 S16384 D64
     // the fetched bytes halve). Elsewhere the order is ascending, as the
     // peeled loop below assumes.
-    const bool backwards = !CAUSAL && !SPLIT && Sk % INTERVAL_KEYS == 0 &&
+    const bool backwards = !CAUSAL && !SPLIT && Sk % G::IKEYS == 0 &&
                            ((blockIdx.x >> 8) & 1u) != 0u;
     auto pos = [&](int x) { return pb + (backwards ? n_int - 1 - x : x); };
 
@@ -878,23 +888,23 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     make_copy_plan<D, VAR>(cp, cw, lane);
     const bool copier = !G::PROD || producer;
     if (copier && n_int > 0)
-      copy_group<D, VAR>(cp.k_off, kh, pos(0) * INTERVAL_KEYS, S, kring, cw);  // K of step 0
+      copy_group<D, VAR>(cp.k_off, kh, pos(0) * G::IKEYS, S, kring, cw);  // K of step 0
     if constexpr (G::PV_SAME) {
       if (copier && n_int > 0)
-        copy_group<D, VAR>(cp.v_off, vh, pos(0) * INTERVAL_KEYS, S, vring, cw);  // V of step 0
+        copy_group<D, VAR>(cp.v_off, vh, pos(0) * G::IKEYS, S, vring, cw);  // V of step 0
     }
     if constexpr (G::PV_SAME && G::BAR2) {
       // four-slot ring: steps 0 and 1 land before the first barrier
       if (n_int > 1) {
-        copy_group<D, VAR>(cp.k_off, kh, pos(1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, cw);
-        copy_group<D, VAR>(cp.v_off, vh, pos(1) * INTERVAL_KEYS, S, vring + G::SLOT_HALVES, cw);
+        copy_group<D, VAR>(cp.k_off, kh, pos(1) * G::IKEYS, S, kring + G::SLOT_HALVES, cw);
+        copy_group<D, VAR>(cp.v_off, vh, pos(1) * G::IKEYS, S, vring + G::SLOT_HALVES, cw);
       }
       wait_copies();
     } else if constexpr (G::PV_SAME && R == 3) {
       // three-slot ring: step 1 is in flight from the start
       if (n_int > 1) {
-        copy_group<D, VAR>(cp.k_off, kh, pos(1) * INTERVAL_KEYS, S, kring + G::SLOT_HALVES, cw);
-        copy_group<D, VAR>(cp.v_off, vh, pos(1) * INTERVAL_KEYS, S, vring + G::SLOT_HALVES, cw);
+        copy_group<D, VAR>(cp.k_off, kh, pos(1) * G::IKEYS, S, kring + G::SLOT_HALVES, cw);
+        copy_group<D, VAR>(cp.v_off, vh, pos(1) * G::IKEYS, S, vring + G::SLOT_HALVES, cw);
         wait_copies_keep<2 * G::LOADS>();
       } else {
         wait_copies();
@@ -913,9 +923,9 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
         for (int j = 0; j < n_int; ++j) {
           if (j + 1 < n_int) {
             const int sl = (j + 1) % R;
-            copy_group<D, VAR>(cp.k_off, kh, pos(j + 1) * INTERVAL_KEYS, S,
+            copy_group<D, VAR>(cp.k_off, kh, pos(j + 1) * G::IKEYS, S,
                                kring + sl * G::SLOT_HALVES, cw);
-            copy_group<D, VAR>(cp.v_off, vh, pos(j + 1) * INTERVAL_KEYS, S,
+            copy_group<D, VAR>(cp.v_off, vh, pos(j + 1) * G::IKEYS, S,
                                vring + sl * G::SLOT_HALVES, cw);
           }
           wait_copies();
@@ -938,10 +948,10 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     // branches.
     auto copies = [&](int j) __attribute__((always_inline)) {
       if (j + 1 < n_int)
-        copy_group<D, VAR>(cp.k_off, kh, pos(j + 1) * INTERVAL_KEYS, S,
+        copy_group<D, VAR>(cp.k_off, kh, pos(j + 1) * G::IKEYS, S,
                       kring + ((j + 1) & 1) * G::SLOT_HALVES, cw);
       if (j < n_int)
-        copy_group<D, VAR>(cp.v_off, vh, pos(j) * INTERVAL_KEYS, S,
+        copy_group<D, VAR>(cp.v_off, vh, pos(j) * G::IKEYS, S,
                       vring + (j & 1) * G::SLOT_HALVES, cw);
       if constexpr (G::SYNC) {
         wait_copies();
@@ -951,7 +961,7 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     // softmax of this wave's tile of interval p (masks possible when EDGE)
     auto softmax_int = [&](int p, auto edge_flag) __attribute__((always_inline)) {
       if constexpr (G::SOFTMAX_PRIO) __builtin_amdgcn_s_setprio(2);
-      const int key0 = pos(p) * INTERVAL_KEYS + phase * G::BN;
+      const int key0 = pos(p) * G::IKEYS + phase * G::BN;
       if constexpr (decltype(edge_flag)::value)
         softmax_any<D, VAR, CAUSAL>(cr, sc, pf, c, key0, qpos0, S, li, g, p == 0);
       else
@@ -984,9 +994,9 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
       auto copies_ahead = [&](int jj) __attribute__((always_inline)) {
         if (!G::PROD && jj + AH < n_int) {
           const int sl = (jj + AH) % R;
-          copy_group<D, VAR>(cp.k_off, kh, pos(jj + AH) * INTERVAL_KEYS, S,
+          copy_group<D, VAR>(cp.k_off, kh, pos(jj + AH) * G::IKEYS, S,
                         kring + sl * G::SLOT_HALVES, cw);
-          copy_group<D, VAR>(cp.v_off, vh, pos(jj + AH) * INTERVAL_KEYS, S,
+          copy_group<D, VAR>(cp.v_off, vh, pos(jj + AH) * G::IKEYS, S,
                         vring + sl * G::SLOT_HALVES, cw);
         }
         if constexpr (G::SYNC) {
@@ -1023,7 +1033,7 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
         constexpr int QS = decltype(qs_flag)::value;
         constexpr int NS = decltype(nside)::value;
         constexpr int NR = decltype(nread)::value;
-        const int key0 = pos(jj) * INTERVAL_KEYS + phase * G::BN;
+        const int key0 = pos(jj) * G::IKEYS + phase * G::BN;
         if constexpr (decltype(edge_flag)::value)
           softmax_any<D, VAR, CAUSAL, QS, QS + 1, NS, NR>(cr, sc, pf, c, key0, qpos0, S, li, g,
                                                           jj == 0, side);
@@ -1173,8 +1183,8 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     // sub-tiles one 16-byte slot {m, d, m, d}, and the output blocks it does
     // not finalise, one slot per block -- each lane at 16 * lane in a slot, so
     // reads and writes are conflict-free. Then each wave merges the NPH
-    // carriers of its query group for its own blocks, db in
-    // [phase * OWN_DB, (phase + 1) * OWN_DB). Block and partner indices are
+    // carriers of its query group for the blocks it owns (owner(db) ==
+    // phase). Block and partner indices are
     // compile-time (unrolled loops with wave-uniform branches on the phase),
     // so no register array is indexed at run time. The last interval ended
     // with a barrier, so the ring is no longer read.
@@ -1196,7 +1206,7 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     for (int qs = 0; qs < QSUB; ++qs)
   #pragma unroll
       for (int db = 0; db < G::D_BLOCKS; ++db)
-        if (db / G::OWN_DB != phase) *o_slot(wave, qs, db) = cr[qs].o[db];
+        if (G::owner(db) != phase) *o_slot(wave, qs, db) = cr[qs].o[db];
     __syncthreads();
 
     float* lse_h = lse + (int64_t)bh * Sq;
@@ -1230,11 +1240,11 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
       if (row < Sq) {
   #pragma unroll
         for (int db = 0; db < G::D_BLOCKS; ++db) {
-          if (db / G::OWN_DB != phase) continue;
+          if (G::owner(db) != phase) continue;
           f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   #pragma unroll
           for (int p = 0; p < NPH; ++p) {
-            if (p == db / G::OWN_DB)
+            if (p == G::owner(db))
               acc += cr[qs].o[db] * w[p];
             else
               acc += *o_slot(qgrp * NPH + p, qs, db) * w[p];

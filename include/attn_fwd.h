@@ -129,6 +129,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                                  /* intervals, four-slot K/V ring                */
 #define ATTN_VARIANT_PROD 64     /* D = 64: four producer waves issue the K/V    */
                                  /* copies (768-thread workgroups)               */
+#define ATTN_VARIANT_TRIO 128    /* D = 64: twelve compute waves, three per SIMD, */
+                                 /* over 192-key intervals                       */
 
 /*
  * attn_fwd_variant -- attn_fwd with a chosen compiled variant of the kernel,
@@ -155,6 +157,9 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *    every K/V copy and only wait and synchronise, so that the eight compute
  *    waves never touch global memory inside the key loop (Part 2, Refused
  *    Optimizations: the producer warp of warp specialisation).
+ *  - ATTN_VARIANT_TRIO: three compute waves per SIMD instead of two (twelve
+ *    per workgroup, three 64-key tiles per barrier interval), for more waves
+ *    to overlap one another's MFMA and softmax phases.
  *  - ATTN_VARIANT_SYNC: a check of the K/V ring protocol rather than an
  *    optimisation: every copy into LDS is waited for and followed by a
  *    workgroup barrier right after it is issued (and D = 128 runs lock-step,
@@ -164,8 +169,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *
  *  q ... causal, stream : as attn_fwd (same layouts, checks and status codes).
  *  variant : one of the ATTN_VARIANT_* values; D = 64 builds 0, RING3,
- *            EXP_POLY, WIDE, SUBPIPE, SYNC, BAR2 and PROD, D = 128 builds 0,
- *            EXP_POLY and SYNC. Any other
+ *            EXP_POLY, WIDE, SUBPIPE, SYNC, BAR2, PROD and TRIO, D = 128
+ *            builds 0, EXP_POLY and SYNC. Any other
  *            value (or combination) returns ATTN_ERR_UNSUPPORTED before
  *            anything is enqueued.
  */

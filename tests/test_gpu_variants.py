@@ -16,9 +16,10 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 # (D, variant) pairs built into the library, besides the default kernel
-BUILT = [(64, 1), (64, 2), (64, 4), (64, 8), (64, 16), (64, 32), (64, 64), (128, 2), (128, 16)]
+BUILT = [(64, 1), (64, 2), (64, 4), (64, 8), (64, 16), (64, 32), (64, 64), (64, 128),
+         (128, 2), (128, 16)]
 NAMES = {1: "ring3", 2: "exp_poly", 4: "wide", 8: "subpipe", 16: "sync", 32: "bar2",
-         64: "prod"}
+         64: "prod", 128: "trio"}
 
 SHAPES = [
     # B, H, S, causal, scale, seed
