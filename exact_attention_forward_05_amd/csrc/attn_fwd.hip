@@ -33,15 +33,14 @@ template <int D, bool CAUSAL, int VAR = 0>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
            int Sq, int Sk, float scale, int n_splits, void* workspace, hipStream_t stream) {
   using namespace attn;
-  // A non-causal single pass at D = 64 runs three compute waves per SIMD
-  // (VAR_TRIO: 2-9% faster there); causal and split launches keep two, where
-  // the 192-key intervals measured no better or worse. The synchronous-copy
-  // check follows the same choice, so that it mirrors the default kernel.
-  if constexpr (D == 64 && !CAUSAL && (VAR == 0 || VAR == VAR_SYNC)) {
-    if (n_splits == 1)
-      return launch<D, CAUSAL, VAR | VAR_TRIO>(q, k, v, o, lse, B, H, Sq, Sk, scale, 1, workspace,
-                                               stream);
-  }
+  // Non-causal launches at D = 64 run three compute waves per SIMD (VAR_TRIO:
+  // 2-9% faster for a single pass, equal split); causal launches keep two,
+  // where the 192-key intervals leave more of the last interval idle. The
+  // synchronous-copy check follows the same choice, so that it mirrors the
+  // default kernel.
+  if constexpr (D == 64 && !CAUSAL && (VAR == 0 || VAR == VAR_SYNC))
+    return launch<D, CAUSAL, VAR | VAR_TRIO>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_splits,
+                                             workspace, stream);
   plan::Launch L;
   const int rc = plan::make_launch(B, H, Sq, D, CAUSAL ? 1 : 0, n_splits, &L, msg());
   if (rc != ATTN_OK) return rc;
@@ -62,12 +61,12 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, VAR>), dim3((unsigned)L.blocks),
                        dim3(WG_THREADS), 0, stream, qh, kh, vh, oh, lse, BH, Sq, Sk, L.n_qtiles, 1,
                        L.order, c, qsign, nullptr, nullptr);
-  } else if constexpr (VAR == 0) {
+  } else if constexpr (VAR == 0 || VAR == VAR_TRIO) {
     float* part_o = static_cast<float*>(workspace);
     float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                plan::part_o_bytes(B, H, Sq, D, n_splits));
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, true>), dim3((unsigned)L.blocks),
-                       dim3(THREADS), 0, stream, qh, kh, vh, oh, lse, BH, Sq, Sk, L.n_qtiles,
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, true, VAR>), dim3((unsigned)L.blocks),
+                       dim3(WG_THREADS), 0, stream, qh, kh, vh, oh, lse, BH, Sq, Sk, L.n_qtiles,
                        n_splits, L.order, c, qsign, part_o, part_lse);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
