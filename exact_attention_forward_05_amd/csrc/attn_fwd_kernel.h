@@ -873,16 +873,17 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     // checked at run time.)
 
     // Key order. Loop step x folds the keys at interval position pos(x). In
-    // a non-causal single pass over whole intervals every wave's live
-    // intervals are all of them and none needs a mask, so the order is free:
-    // there, every other round of 32 workgroups per XCD (workgroup ids are
-    // dealt round-robin to 8 XCDs) walks the keys backwards and starts on the
-    // K/V that the round before it left in the XCD's L2 (at B1 H8 S16384 D64
-    // the fetched bytes halve). Elsewhere the order is ascending, as the
-    // peeled loop below assumes.
-    const bool backwards = !CAUSAL && !SPLIT && Sk % G::IKEYS == 0 &&
-                           ((blockIdx.x >> 8) & 1u) != 0u;
-    auto pos = [&](int x) { return pb + (backwards ? n_int - 1 - x : x); };
+    // a non-causal single pass every wave is live in every interval but
+    // possibly the last (the sequence tail, the only one with masks), so the
+    // order of the others is free: there, every other round of 32 workgroups
+    // per XCD (workgroup ids are dealt round-robin to 8 XCDs) walks them
+    // backwards, starting on the K/V that the round before it left in the
+    // XCD's L2 (at B1 H8 S16384 D64 the fetched bytes halve), and still ends
+    // on the last interval. Elsewhere the order is ascending.
+    const bool backwards = !CAUSAL && !SPLIT && ((blockIdx.x >> 8) & 1u) != 0u;
+    auto pos = [&](int x) {
+      return pb + (backwards && x < n_int - 1 ? n_int - 2 - x : x);
+    };
 
     CopyPlan<D, VAR> cp;
     make_copy_plan<D, VAR>(cp, cw, lane);
