@@ -90,6 +90,7 @@ enum : int {
   VAR_BAR2 = 32,     // D = 64: one workgroup barrier per two key intervals (four-slot ring)
   VAR_PROD = 64,     // D = 64: four producer waves issue every K/V copy
   VAR_TRIO = 128,    // D = 64: three waves per SIMD over three 64-key tiles per interval
+  VAR_QUAD = 256,    // D = 64: four waves per SIMD over four 32-key tiles per interval
 };
 
 template <int D, int VAR = 0>
@@ -103,8 +104,11 @@ struct Geometry {
   // query group, each on its own 64-key tile of a 192-key interval (three
   // 159-VGPR allocations fit a SIMD's 512 registers per lane).
   static constexpr bool TRIO = D == 64 && (VAR & VAR_TRIO) != 0;
-  static constexpr int NPH = WIDE ? 4 : TRIO ? 3 : 2;
-  static constexpr int CWAVES = TRIO ? 12 : WAVES;         // compute waves
+  // Four waves per SIMD (VAR_QUAD, D = 64): sixteen compute waves, four per
+  // query group on 32-key tiles of a 128-key interval, at most 128 VGPRs.
+  static constexpr bool QUAD = D == 64 && (VAR & VAR_QUAD) != 0;
+  static constexpr int NPH = (WIDE || QUAD) ? 4 : TRIO ? 3 : 2;
+  static constexpr int CWAVES = TRIO ? 12 : QUAD ? 16 : WAVES;  // compute waves
   static constexpr int QGROUPS = CWAVES / NPH;             // query groups
   static constexpr int ROWS = BLOCK_M / QGROUPS;           // query rows per wave
   static constexpr int QSUB = ROWS / 16;                   // 16-row query sub-tiles per wave
@@ -181,6 +185,7 @@ struct Geometry {
   static_assert(D % 64 == 0, "D must be a multiple of 64");
   static_assert(LOADS * 64 * NCOP == PIECES, "tiling");
   static_assert(!PROD || VAR == VAR_PROD, "producer waves run the default two-slot ring alone");
+  static_assert(!QUAD || VAR == VAR_QUAD, "four waves per SIMD run the default order alone");
   static_assert(!TRIO || (VAR & ~VAR_SYNC) == VAR_TRIO,
                 "three waves per SIMD run the default order (or its synchronous-copy check)");
   static_assert(QSUB * 16 * QGROUPS == BLOCK_M && KB >= 2 && KC >= 1, "geometry");
@@ -394,7 +399,7 @@ __device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
   constexpr int NPV = PV ? G::KC * G::D_BLOCKS : 0;
   constexpr int NQK = QK ? G::KB * G::D_CHUNKS : 0;
   constexpr int NU = NPV + NQK;
-  constexpr int AHEAD_MAX = D == 64 ? 8 : 4;
+  constexpr int AHEAD_MAX = G::QUAD ? 4 : D == 64 ? 8 : 4;
   constexpr int AHEAD = AHEAD_MAX < NU ? AHEAD_MAX : NU;
   // V^T operand (d block db, key chunk kc): lane (i, g) needs
   // V[32kc + 8g + e][16db + i], e = 0..7 -- two transposing reads over 4 key

@@ -131,6 +131,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                                  /* copies (768-thread workgroups)               */
 #define ATTN_VARIANT_TRIO 128    /* D = 64: twelve compute waves, three per SIMD, */
                                  /* over 192-key intervals                       */
+#define ATTN_VARIANT_QUAD 256    /* D = 64: sixteen compute waves, four per SIMD, */
+                                 /* on 32-key tiles                              */
 
 /*
  * attn_fwd_variant -- attn_fwd with a chosen compiled variant of the kernel,
@@ -160,6 +162,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *  - ATTN_VARIANT_TRIO: three compute waves per SIMD instead of two (twelve
  *    per workgroup, three 64-key tiles per barrier interval), for more waves
  *    to overlap one another's MFMA and softmax phases.
+ *  - ATTN_VARIANT_QUAD: four compute waves per SIMD (sixteen per workgroup,
+ *    four 32-key tiles per 128-key interval, at most 128 VGPRs per wave).
  *  - ATTN_VARIANT_SYNC: a check of the K/V ring protocol rather than an
  *    optimisation: every copy into LDS is waited for and followed by a
  *    workgroup barrier right after it is issued (and D = 128 runs lock-step,
@@ -169,8 +173,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *
  *  q ... causal, stream : as attn_fwd (same layouts, checks and status codes).
  *  variant : one of the ATTN_VARIANT_* values; D = 64 builds 0, RING3,
- *            EXP_POLY, WIDE, SUBPIPE, SYNC, BAR2, PROD and TRIO, D = 128
- *            builds 0, EXP_POLY and SYNC. Any other
+ *            EXP_POLY, WIDE, SUBPIPE, SYNC, BAR2, PROD, TRIO and QUAD,
+ *            D = 128 builds 0, EXP_POLY and SYNC. Any other
  *            value (or combination) returns ATTN_ERR_UNSUPPORTED before
  *            anything is enqueued.
  */

@@ -17,9 +17,9 @@ pytestmark = [pytest.mark.gpu,
 
 # (D, variant) pairs built into the library, besides the default kernel
 BUILT = [(64, 1), (64, 2), (64, 4), (64, 8), (64, 16), (64, 32), (64, 64), (64, 128),
-         (128, 2), (128, 16)]
+         (64, 256), (128, 2), (128, 16)]
 NAMES = {1: "ring3", 2: "exp_poly", 4: "wide", 8: "subpipe", 16: "sync", 32: "bar2",
-         64: "prod", 128: "trio"}
+         64: "prod", 128: "trio", 256: "quad"}
 
 SHAPES = [
     # B, H, S, causal, scale, seed
