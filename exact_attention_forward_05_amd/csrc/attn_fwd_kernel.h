@@ -77,6 +77,11 @@ constexpr float NEG_BIG = -1.0e30f;   // finite stand-in for -infinity
 // Lazy-max bound on a lane's tile sum: every probability stays below it, and
 // so below fp16's largest finite value (65504) with room for rounding.
 constexpr float P_LIMIT = 32768.0f;
+// A redo after the first step of a tile sets the running max this far (log2
+// units) above the tile's max, so that a row whose max keeps climbing (peaked
+// scores) redoes less often; the probabilities then start at most 2^-8, still
+// normal in fp16. The first step takes the exact max.
+constexpr float MAX_HEADROOM = 8.0f;
 constexpr uint32_t BUF_FLAGS = 0x00020000u;  // raw buffer, 32-bit data format
 
 // Compile-time variants of the kernel (bit flags), selectable through
@@ -704,7 +709,7 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
         tmax = __builtin_fmaxf(tmax, max4(s));
       }
       tmax = group_max(tmax);
-      const float m_new = __builtin_fmaxf(cr[qs].m, tmax * c);
+      const float m_new = __builtin_fmaxf(cr[qs].m, tmax * c + (first ? 0.0f : MAX_HEADROOM));
       const float alpha = __builtin_amdgcn_exp2f(cr[qs].m - m_new);
       cr[qs].d *= alpha;
 #pragma unroll
