@@ -8,16 +8,17 @@
 // remark of the wrap-up). The layout below is designed for CDNA4 rather than
 // translated from the page's mma.sync listings.
 //
-// Work decomposition. A workgroup of 8 waves owns BLOCK_M = 128 query rows of
-// one (batch, head) and streams the keys in intervals of 128, which arrive in
-// LDS as NPH = 2 tiles of BN = 64 keys. The waves form QGROUPS = 4 query
+// Work decomposition. A workgroup owns BLOCK_M = 128 query rows of one
+// (batch, head) and streams the keys in intervals of NPH tiles of BN keys,
+// which arrive in LDS together. Its compute waves form QGROUPS = 4 query
 // groups of 32 rows (two 16-row sub-tiles per wave); the NPH waves of a group
 // take one tile each per interval (wave phase p folds tiles p, p + NPH, ...).
-// Wave w runs on SIMD w % 4, so the two waves on one SIMD hold different
-// query rows and fill each other's stalls. (VAR_WIDE at D = 64: NPH = 4
-// tiles of 32 keys, 2 query groups of 64 rows.) At the end the NPH carriers of
-// a query group meet in LDS and each wave merges them for its share of the
-// output columns.
+// Wave w runs on SIMD w % 4, so the waves sharing a SIMD hold different query
+// rows and fill each other's stalls. Default: 8 waves, NPH = 2 tiles of 64
+// keys (two waves per SIMD); at D = 64 without the causal mask VAR_TRIO runs
+// 12 waves, NPH = 3 (three per SIMD). Other geometries are variants (see
+// Geometry). At the end the NPH carriers of a query group meet in LDS and each
+// wave merges them for the output columns it owns.
 //
 // MFMA: v_mfma_f32_16x16x32_f16. Lane l = 16*g + i (g = 0..3, i = 0..15):
 //   A: row i, contraction slots (g, 0..7); B: column i, slots (g, 0..7);
@@ -38,14 +39,15 @@
 // The running max is updated lazily: a tile is first exponentiated against the
 // current m; only if some lane's probabilities could overflow (their fp16 sum
 // exceeds P_LIMIT, or is not finite) does the wave compute the tile max,
-// rescale o and d, and redo the tile, for the 16-row sub-tiles concerned.
-// Because o and d always share one m, the result is the same softmax; m never
-// exceeds the true row max, and probabilities up to P_LIMIT keep fp16's
-// relative precision. The row sum adds the fp16-rounded probabilities
-// (v_dot2), so d normalises exactly the weights the P.V product used.
+// rescale o and d, and redo the tile, for the 16-row sub-tiles concerned (the
+// first step of a tile takes the max up front; later redos leave a headroom
+// of MAX_HEADROOM above it). Because o and d always share one m, the result is
+// the same softmax, and probabilities up to P_LIMIT keep fp16's relative
+// precision. The row sum adds the fp16-rounded probabilities (v_dot2), so d
+// normalises exactly the weights the P.V product used.
 //
 // LDS. K and V tiles arrive by direct global->LDS loads into two-slot rings
-// of tile pairs, one barrier interval before they are read. K rows are stored in
+// of tile groups, one barrier interval before they are read. K rows are stored in
 // MFMA-row order (row 16*kb + i holds key st_key(kb, i)), V rows in key order;
 // both are unpadded with XOR-permuted 16-byte chunks so that every operand
 // read is free of bank conflicts on the 64-bank LDS. V^T operands come from
