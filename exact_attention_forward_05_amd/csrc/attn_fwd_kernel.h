@@ -140,9 +140,10 @@ struct Geometry {
   static constexpr int RING = BAR2 ? 4 : (D == 64 && (VAR & VAR_RING3) != 0) ? 3 : 2;
   static constexpr int AHEAD = BAR2 ? 2 : RING - 1;  // intervals between a copy and its use
   static constexpr int SLOT_HALVES = NPH * K_HALVES;        // one interval's tiles
-  // At D = 128 the Q fragments would not fit the register budget next to the
-  // output accumulators: the workgroup's Q rows are staged in LDS instead.
-  static constexpr bool Q_IN_LDS = D == 128;
+  // Q^T fragments stay in registers for the whole key loop at both head
+  // dimensions. (At D = 128 they were staged in LDS and re-read each interval
+  // while the kernel needed 250 VGPRs; at 236 with them in registers it runs
+  // 1-2% faster and reads 64 KB less from LDS per interval and CU.)
   // The second wave of each SIMD (waves 4-7) runs half an interval out of
   // phase with the first (softmax against the other wave's MFMA phase). This
   // pays only where the MFMA phase is long next to the softmax: at D = 128
@@ -174,7 +175,6 @@ struct Geometry {
   // of 3, 6, 10 and 16; fp32-add row sums in place of v_dot2 did not help).
   static constexpr bool SUBPIPE = D == 64 && (VAR & VAR_SUBPIPE) != 0 && QSUB == 2;
   static constexpr int SIDE_VPER = 3;
-  static constexpr int Q_HALVES = Q_IN_LDS ? BLOCK_M * D : 0;
   static constexpr int D_CHUNKS = D / 32;                  // contraction chunks of Q.K
   static constexpr int D_BLOCKS = D / 16;                  // 16-row blocks of O^T
   // Producer waves (VAR_PROD, D = 64): the workgroup gets four more waves,
@@ -205,7 +205,7 @@ struct Geometry {
   static constexpr int MD_SLOTS = (QSUB + 1) / 2;
   static constexpr int HANDOFF_SLOTS = MD_SLOTS + QSUB * D_BLOCKS;
   static constexpr int HANDOFF_BYTES = CWAVES * HANDOFF_SLOTS * 64 * 16;
-  static constexpr int LOOP_BYTES = (2 * RING * SLOT_HALVES + Q_HALVES) * 2;
+  static constexpr int LOOP_BYTES = 2 * RING * SLOT_HALVES * 2;
   static constexpr int LDS_BYTES = LOOP_BYTES > HANDOFF_BYTES ? LOOP_BYTES : HANDOFF_BYTES;
   static constexpr int LDS_HALVES = LDS_BYTES / 2;
   static_assert(D_BLOCKS >= NPH, "every wave of a query group owns an output block");
@@ -398,9 +398,7 @@ __device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
                                            ScoreSet<D, VAR>& sc,
                                            const QSet<D, VAR>& qf,
                                            const _Float16* __restrict__ vtile,
-                                           const _Float16* __restrict__ ktile,
-                                           const _Float16* __restrict__ qtile, uint32_t qsign,
-                                           int li, int g) {
+                                           const _Float16* __restrict__ ktile, int li, int g) {
   using G = Geometry<D, VAR>;
   constexpr int QSUB = G::QSUB;
   constexpr int NPV = PV ? G::KC * G::D_BLOCKS : 0;
@@ -418,30 +416,6 @@ __device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
   const int vx = (li & 3) >> 1;
   // K operand (key block kb, d chunk ch): row 16kb + li, halves 32ch + 8g.
   const int ksw = k_swizzle<D>(li);  // the swizzle bits of row 16*kb + li do not depend on kb
-  // Q^T fragments: from registers, or (Q_IN_LDS) read from the LDS Q tile at
-  // the start of the phase -- row 16qs + li of the wave's rows, halves
-  // 32ch + 8g, chunks permuted like K rows.
-  f16x8 ql[QSUB][G::D_CHUNKS];
-  if constexpr (G::Q_IN_LDS && QK) {
-#pragma unroll
-    for (int qs = 0; qs < QSUB; ++qs)
-#pragma unroll
-      for (int ch = 0; ch < G::D_CHUNKS; ++ch) {
-        const int row = 16 * qs + li;
-        ql[qs][ch] = *reinterpret_cast<const f16x8*>(qtile + row * D +
-                                                     8 * ((4 * ch + g) ^ k_swizzle<D>(row)));
-      }
-    if (qsign != 0u) {  // negative scale: flip Q's sign (exact)
-#pragma unroll
-      for (int qs = 0; qs < QSUB; ++qs)
-#pragma unroll
-        for (int ch = 0; ch < G::D_CHUNKS; ++ch)
-          ql[qs][ch] = __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, ql[qs][ch]) ^ qsign);
-    }
-  }
-  auto qfrag = [&](int qs, int ch) -> const f16x8& {
-    if constexpr (G::Q_IN_LDS) return ql[qs][ch]; else return qf[qs][ch];
-  };
   auto load = [&](int u) -> f16x8 {
     if (u < NPV) {
       const int kc = u / G::D_BLOCKS, db = u % G::D_BLOCKS;
@@ -464,7 +438,7 @@ __device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
 #pragma unroll
       for (int qs = 0; qs < QSUB; ++qs)
         sc[qs][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            a, qfrag(qs, ch), ch == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[qs][kb], 0, 0, 0);
+            a, qf[qs][ch], ch == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[qs][kb], 0, 0, 0);
     }
   };
   f16x8 fr[NU];
@@ -772,7 +746,6 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
   __shared__ __attribute__((aligned(16))) _Float16 smem[G::LDS_HALVES];
   _Float16* kring = smem;                           // [slot][tile] K tiles
   _Float16* vring = smem + R * G::SLOT_HALVES;      // [slot][tile] V tiles
-  _Float16* qtile = smem + 2 * R * G::SLOT_HALVES;  // Q rows of the workgroup (Q_IN_LDS)
 
   const int split = SPLIT ? (int)(blockIdx.x % (unsigned)n_splits) : 0;
   const int bid = SPLIT ? (int)(blockIdx.x / (unsigned)n_splits) : (int)blockIdx.x;
@@ -813,27 +786,12 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     const int qrow0 = q0 + G::ROWS * qgrp;  // this wave's first query row
     const int qpos0 = qrow0 + koff;         // its sequence position
 
-    // Q^T fragments, loaded once (sign-flipped when the scale is negative):
-    // into registers, or (Q_IN_LDS) the workgroup's Q rows into LDS by direct
-    // copies, chunks permuted like K rows; rows past S read as zeros.
+    // Q^T fragments, loaded once into registers (sign-flipped when the scale
+    // is negative); rows past S_q read as zeros (outside the descriptor's
+    // range; offsets are unsigned 32-bit, S_q * D * 2 < 2^31).
     f16x8 qf[QSUB][G::D_CHUNKS];
     if (producer) {
       // no query rows
-    } else if constexpr (G::Q_IN_LDS) {
-      constexpr int UNITS = BLOCK_M * D * 2 / 1024;  // 1 KB copy units
-      static_assert(UNITS % WAVES == 0, "Q copy split");
-  #pragma unroll
-      for (int i = 0; i < UNITS / WAVES; ++i) {
-        const int unit = i * WAVES + wave;
-        const int slot = unit * 64 + lane;
-        const int row = slot / (D / 8);
-        const int pc = slot % (D / 8);
-        // Rows past S (up to S + 127) fall outside the descriptor's range and
-        // read as zeros; offsets are unsigned 32-bit (S * D * 2 < 2^31).
-        const uint32_t off = ((uint32_t)(q0 + row) * D + 8u * (uint32_t)(pc ^ k_swizzle<D>(row))) * 2u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            qrs, (__attribute__((address_space(3))) void*)(qtile + unit * 512), 16, off, 0, 0, 0);
-      }
     } else {
   #pragma unroll
       for (int qs = 0; qs < QSUB; ++qs) {
@@ -847,7 +805,6 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
         }
       }
     }
-    const _Float16* qwave = qtile + G::ROWS * qgrp * D;  // this wave's rows in the LDS Q tile
 
     Carrier<D> cr[QSUB];
   #pragma unroll
@@ -986,7 +943,7 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
       constexpr bool QK = decltype(qk_flag)::value;
       const _Float16* kslot = kring + (j & 1) * G::SLOT_HALVES + phase * G::K_HALVES;
       const _Float16* vslot = vring + ((j + 1) & 1) * G::SLOT_HALVES + phase * G::V_HALVES;
-      if constexpr (PV || QK) mfma_phase<D, VAR, PV, QK>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+      if constexpr (PV || QK) mfma_phase<D, VAR, PV, QK>(cr, pf, sc, qf, vslot, kslot, li, g);
     };
     auto end_interval = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
@@ -1095,13 +1052,13 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
         const int slot = SL >= 0 ? SL : jj % R;
         const _Float16* kslot = kring + slot * G::SLOT_HALVES + phase * G::K_HALVES;
         const _Float16* vslot = vring + slot * G::SLOT_HALVES + phase * G::V_HALVES;
-        mfma_phase<D, VAR, false, true>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+        mfma_phase<D, VAR, false, true>(cr, pf, sc, qf, vslot, kslot, li, g);
         __builtin_amdgcn_sched_barrier(0);
         copies_ahead(jj);
         __builtin_amdgcn_sched_barrier(0);
         softmax_int(jj, edge_flag);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_phase<D, VAR, true, false>(cr, pf, sc, qf, vslot, kslot, qwave, qsign, li, g);
+        mfma_phase<D, VAR, true, false>(cr, pf, sc, qf, vslot, kslot, li, g);
         end_int(jj);
       };
       using S0 = std::integral_constant<int, 0>;
