@@ -29,19 +29,26 @@ thread_local char g_last_error[512] = "";
 
 attn::plan::Msg msg() { return attn::plan::Msg{g_last_error, sizeof(g_last_error)}; }
 
+// Keys per head from which a non-causal D = 64 launch runs three compute waves
+// per SIMD.
+constexpr int TRIO_MIN_KEYS = 2048;
+
 // Sq query rows against Sk keys per head (Sq == Sk for self-attention).
 template <int D, bool CAUSAL, int VAR = 0>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
            int Sq, int Sk, float scale, int n_splits, void* workspace, hipStream_t stream) {
   using namespace attn;
-  // Non-causal launches at D = 64 run three compute waves per SIMD (VAR_TRIO:
-  // 2-9% faster for a single pass, equal split); causal launches keep two,
-  // where the 192-key intervals leave more of the last interval idle. The
-  // synchronous-copy check follows the same choice, so that it mirrors the
-  // default kernel.
-  if constexpr (D == 64 && !CAUSAL && (VAR == 0 || VAR == VAR_SYNC))
-    return launch<D, CAUSAL, VAR | VAR_TRIO>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_splits,
-                                             workspace, stream);
+  // Non-causal launches at D = 64 over at least 2048 keys run three compute
+  // waves per SIMD (VAR_TRIO: 1.5-9% faster for a single pass, equal split);
+  // shorter ones (3-14% slower there: one or two 192-key intervals, the last
+  // partly idle) and causal launches (more of each tile's last interval idle)
+  // keep two. The synchronous-copy check follows the same choice, so that it
+  // mirrors the default kernel.
+  if constexpr (D == 64 && !CAUSAL && (VAR == 0 || VAR == VAR_SYNC)) {
+    if (Sk >= TRIO_MIN_KEYS)
+      return launch<D, CAUSAL, VAR | VAR_TRIO>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_splits,
+                                               workspace, stream);
+  }
   plan::Launch L;
   const int rc = plan::make_launch(B, H, Sq, D, CAUSAL ? 1 : 0, n_splits, &L, msg());
   if (rc != ATTN_OK) return rc;

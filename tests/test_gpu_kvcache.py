@@ -46,6 +46,9 @@ CASES = [
     (1, 2, 200, 150, 64, False, 2, 8),      # S_q > S_k without a mask
     (3, 2, 1, 1, 128, True, 1, 9),          # one key
     (1, 2, 16, 4096, 64, True, 64, 10),     # more runs than keys for early rows
+    # non-causal D = 64 from 2048 keys: three waves per SIMD, key tails
+    (1, 2, 300, 5000, 64, False, 1, 11),
+    (2, 2, 130, 4100, 64, False, 3, 12),
 ]
 
 
