@@ -161,6 +161,15 @@ struct Geometry {
   // waves then interleave shorter MFMA phases with their softmaxes (1-3%
   // faster). At D = 128 the ping-pong order measured faster than this.
   static constexpr bool PV_SAME = D == 64;
+  // Row sums of the probabilities. At D = 64, dot products of the rounded
+  // fp16 values with ones (v_dot2). In the D = 128 ping-pong a softmax runs
+  // beside the other wave's MFMA phase, and a v_dot2 there waits for the
+  // MFMA pipe: one wave issuing MFMAs back to back and one issuing v_dot2
+  // take as long as both run one after the other, while fp32 adds, FMAs and
+  // exponentials beside an MFMA stream lose only 20-35% of their rate
+  // (probe of two waves per SIMD). So D = 128 adds the unrounded fp32
+  // probabilities (4-6% faster there, 2-4% slower at D = 64).
+  static constexpr bool ADD_SUMS = D == 128;
   // A wave in its softmax raises its issue priority (s_setprio), so that the
   // SIMD's other wave, in its MFMA phase or later in its own softmax, does not
   // starve it (2-3% on every workload).
@@ -451,10 +460,13 @@ __device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
   }
   // Pin that order for the scheduler: the reads of the first AHEAD units,
   // then per unit the reads of unit u + AHEAD followed by unit u's two MFMAs.
-  if constexpr (D == 64) {
-    pin_reads<0, AHEAD, NPV>();
-    pin_units<0, NU, NPV, AHEAD, QSUB>();
-  }
+  // Left to itself at D = 128, the scheduler reads most fragments just
+  // before their MFMAs (fewer live registers), so the phase waits on LDS
+  // latency unit after unit and the other wave's softmax fills the gaps;
+  // pinned, the MFMAs issue back to back (with the fp32-add row sums 4-6%
+  // faster; with v_dot2 sums 2-5% slower, as their softmax then waits).
+  pin_reads<0, AHEAD, NPV>();
+  pin_units<0, NU, NPV, AHEAD, QSUB>();
 }
 
 // Operand fragments of one tile for the sub-tile pipelined interval
@@ -612,11 +624,12 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
         }
       }
     }
-  // Row sums of the rounded probabilities, by dot products with ones. With
-  // SUM_ONTO_D (D = 64) a sub-tile's sum is one chain started from the
-  // lane's denominator (dnew, whose excess over d is the tile's sum); else
-  // two chains from zero (tsum), added onto d afterwards. The tile's sum is
-  // tested against the lazy-max bound.
+  // Row sums: dot products of the rounded probabilities with ones, or (with
+  // ADD_SUMS) fp32 adds of the unrounded ones. With SUM_ONTO_D (D = 64) a
+  // sub-tile's sum is one chain started from the lane's denominator (dnew,
+  // whose excess over d is the tile's sum); else two chains from zero
+  // (tsum), added onto d afterwards. The tile's sum is tested against the
+  // lazy-max bound.
   constexpr bool SUM_ONTO_D = G::PV_SAME;
   float dnew[QSUB], tsum[QSUB];
   auto expo = [&](int qs) {
@@ -634,13 +647,22 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
         h[4 + r] = (_Float16)p[2 * kc + 1][r];
       }
       pf[qs][kc] = h;
+      if constexpr (G::ADD_SUMS) {
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int a = SUM_ONTO_D ? 0 : (e >> 1) & 1;
-        acc[a] = __builtin_amdgcn_fdot2(f16x2{h[e], h[e + 1]},
-                                        f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc[a], false);
+        for (int r = 0; r < 4; ++r) {
+          acc[0] += p[2 * kc][r];
+          acc[1] += p[2 * kc + 1][r];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int a = SUM_ONTO_D ? 0 : (e >> 1) & 1;
+          acc[a] = __builtin_amdgcn_fdot2(f16x2{h[e], h[e + 1]},
+                                          f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc[a], false);
+        }
       }
     }
+    static_assert(!(SUM_ONTO_D && G::ADD_SUMS), "one fp32 chain per sub-tile with v_dot2 only");
     if (SUM_ONTO_D)
       dnew[qs] = acc[0];
     else
