@@ -29,9 +29,11 @@ thread_local char g_last_error[512] = "";
 
 attn::plan::Msg msg() { return attn::plan::Msg{g_last_error, sizeof(g_last_error)}; }
 
-// Keys per head from which a non-causal D = 64 launch runs three compute waves
-// per SIMD.
+// Keys per head from which a D = 64 launch runs three compute waves per SIMD:
+// non-causal, and causal single passes whose tiles are not folded into pairs;
+// folded causal single passes from TRIO_MIN_KEYS_FOLDED keys.
 constexpr int TRIO_MIN_KEYS = 2048;
+constexpr int TRIO_MIN_KEYS_FOLDED = 8192;
 
 // Sq query rows against Sk keys per head (Sq == Sk for self-attention).
 template <int D, bool CAUSAL, int VAR = 0>
@@ -41,11 +43,18 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   // Non-causal launches at D = 64 over at least 2048 keys run three compute
   // waves per SIMD (VAR_TRIO: 1.5-9% faster for a single pass, equal split);
   // shorter ones (3-14% slower there: one or two 192-key intervals, the last
-  // partly idle) and causal launches (more of each tile's last interval idle)
-  // keep two. The synchronous-copy check follows the same choice, so that it
-  // mirrors the default kernel.
-  if constexpr (D == 64 && !CAUSAL && (VAR == 0 || VAR == VAR_SYNC)) {
-    if (Sk >= TRIO_MIN_KEYS)
+  // partly idle) keep two. Causal single passes run three waves when their
+  // tiles are not folded (B1 H8 S4096 3.9% faster) or from 8192 keys when
+  // they are (1-2.5% faster; at 4096 keys 1.7% slower, at 1024 13%: a folded
+  // pair's two diagonal intervals leave more of a 192-key interval idle);
+  // causal split runs keep two (mixed, -8% to +3%). The synchronous-copy
+  // check follows the same choice, so that it mirrors the default kernel.
+  if constexpr (D == 64 && (VAR == 0 || VAR == VAR_SYNC)) {
+    const bool trio =
+        !CAUSAL ? Sk >= TRIO_MIN_KEYS
+                : n_splits == 1 && Sk >= (plan::folds(B, H, Sq, 1, n_splits) ? TRIO_MIN_KEYS_FOLDED
+                                                                             : TRIO_MIN_KEYS);
+    if (trio)
       return launch<D, CAUSAL, VAR | VAR_TRIO>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_splits,
                                                workspace, stream);
   }
@@ -69,7 +78,7 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, VAR>), dim3((unsigned)L.blocks),
                        dim3(WG_THREADS), 0, stream, qh, kh, vh, oh, lse, BH, Sq, Sk, L.n_qtiles, 1,
                        L.order, c, qsign, nullptr, nullptr);
-  } else if constexpr (VAR == 0 || VAR == VAR_TRIO) {
+  } else if constexpr (VAR == 0 || (VAR == VAR_TRIO && !CAUSAL)) {
     float* part_o = static_cast<float*>(workspace);
     float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                plan::part_o_bytes(B, H, Sq, D, n_splits));
@@ -88,6 +97,8 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
       hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)L.combine_blocks),
                          dim3(plan::COMBINE_THREADS), 0, stream, part_o, part_lse, oh, lse, rows,
                          n_splits);
+  } else {
+    return plan::fail(msg(), ATTN_ERR_UNSUPPORTED, "split runs of kernel variant %d are not built", VAR);
   }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess)

@@ -111,6 +111,13 @@ struct Launch {
   int combine_runs;        // 1: the wave-per-row combine (few rows), 0: thread per row
 };
 
+// Whether a single-pass causal launch folds its query tiles into mirror pairs
+// (ORDER_FOLDED): when the pairs alone fill the CUs.
+inline bool folds(int B, int H, int Sq, int causal, int n_splits) {
+  const int64_t n_qtiles = ((int64_t)Sq + BLOCK_M - 1) / BLOCK_M;
+  return causal && n_splits == 1 && (int64_t)B * H * ((n_qtiles + 1) / 2) >= FOLD_MIN_WORKGROUPS;
+}
+
 // Launch geometry of one call; ATTN_ERR_SHAPE if a grid does not fit a
 // dispatch. Arguments are already checked.
 inline int make_launch(int B, int H, int Sq, int D, int causal, int n_splits, Launch* out,
@@ -122,12 +129,10 @@ inline int make_launch(int B, int H, int Sq, int D, int causal, int n_splits, La
   // tile pairs: folded mirror pairs equalise them when there are enough to
   // fill the CUs, else the heaviest tiles go first.
   int order = ORDER_TILES;
-  if (n_splits == 1) {
-    if (!causal)
-      order = ORDER_HEADS;
-    else if (BH * ((n_qtiles + 1) / 2) >= FOLD_MIN_WORKGROUPS)
-      order = ORDER_FOLDED;
-  }
+  if (n_splits == 1 && !causal)
+    order = ORDER_HEADS;
+  else if (folds(B, H, Sq, causal, n_splits))
+    order = ORDER_FOLDED;
   const int64_t per_head = order == ORDER_FOLDED ? (n_qtiles + 1) / 2 : n_qtiles;
   const int64_t blocks = BH * per_head * n_splits;
   // (This also keeps workgroup ids, which the work order handles as ints,

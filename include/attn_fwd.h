@@ -162,9 +162,10 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *  - ATTN_VARIANT_TRIO: three compute waves per SIMD instead of two (twelve
  *    per workgroup, three 64-key tiles per barrier interval), for more waves
  *    to overlap one another's MFMA and softmax phases. attn_fwd, the split
- *    and the cache entry points run this geometry at D = 64 without the
- *    causal mask (it is the default there); the variant also builds it
- *    causal, for comparison.
+ *    and the cache entry points run this geometry by default at D = 64 from
+ *    2048 keys without the causal mask, and with it for single passes (from
+ *    8192 keys when the query tiles are folded into mirror pairs); the
+ *    variant runs it for any shape, for comparison.
  *  - ATTN_VARIANT_QUAD: four compute waves per SIMD (sixteen per workgroup,
  *    four 32-key tiles per 128-key interval, at most 128 VGPRs per wave).
  *  - ATTN_VARIANT_SYNC: a check of the K/V ring protocol rather than an

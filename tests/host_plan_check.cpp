@@ -125,6 +125,13 @@ int main() {
                     (long long)blocks);
               CHECK(L.blocks * plan::THREADS <= plan::MAX_WORK_ITEMS, "grid too large\n");
               CHECK(L.n_qtiles == nq, "n_qtiles\n");
+              // folded mirror pairs exactly for causal single passes whose
+              // pairs fill the CUs (the three-wave routing reads folds())
+              const bool want_fold = causal && ns == 1 &&
+                                     (int64_t)B * H * ((nq + 1) / 2) >= plan::FOLD_MIN_WORKGROUPS;
+              CHECK((L.order == ORDER_FOLDED) == want_fold &&
+                        plan::folds(B, H, S, causal, ns) == want_fold,
+                    "fold order B=%d H=%d S=%d causal=%d ns=%d\n", B, H, S, causal, ns);
               CHECK(ns == 1 || (L.combine_blocks >= 1 &&
                                 L.combine_blocks <= plan::COMBINE_MAX_BLOCKS),
                     "combine grid %lld\n", (long long)L.combine_blocks);

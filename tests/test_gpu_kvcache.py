@@ -49,6 +49,9 @@ CASES = [
     # non-causal D = 64 from 2048 keys: three waves per SIMD, key tails
     (1, 2, 300, 5000, 64, False, 1, 11),
     (2, 2, 130, 4100, 64, False, 3, 12),
+    # causal single pass at D = 64 from 2048 keys, tiles not folded: three
+    # waves per SIMD with the query block at the end of the keys
+    (1, 2, 300, 5000, 64, True, 1, 13),
 ]
 
 

@@ -116,6 +116,9 @@ SYNC_SHAPES = [
     (1, 2, 1000, 64, False),
     (1, 16, 4096, 64, True),
     (1, 64, 1024, 64, False),
+    # causal three waves per SIMD: tiles not folded; folded from 8192 keys
+    (1, 8, 4096, 64, True),
+    (1, 8, 8192, 64, True),
     (2, 3, 300, 128, True),
     (1, 2, 1000, 128, False),
     (1, 16, 4096, 128, True),
