@@ -161,15 +161,19 @@ struct Geometry {
   // waves then interleave shorter MFMA phases with their softmaxes (1-3%
   // faster). At D = 128 the ping-pong order measured faster than this.
   static constexpr bool PV_SAME = D == 64;
-  // Row sums of the probabilities. At D = 64, dot products of the rounded
-  // fp16 values with ones (v_dot2). In the D = 128 ping-pong a softmax runs
+  // Row sums of the rounded fp16 probabilities (the weights P.V uses, so that
+  // a row dominated by one key gets exactly that key's V row). At D = 64,
+  // dot products with ones (v_dot2). In the D = 128 ping-pong a softmax runs
   // beside the other wave's MFMA phase, and a v_dot2 there waits for the
   // MFMA pipe: one wave issuing MFMAs back to back and one issuing v_dot2
-  // take as long as both run one after the other, while fp32 adds, FMAs and
+  // take as long as both run one after the other, while adds, FMAs and
   // exponentials beside an MFMA stream lose only 20-35% of their rate
-  // (probe of two waves per SIMD). So D = 128 adds the unrounded fp32
-  // probabilities (4-6% faster there, 2-4% slower at D = 64).
-  static constexpr bool ADD_SUMS = D == 128;
+  // (probe of two waves per SIMD). So D = 128 adds each value with
+  // v_fma_mix_f32 (fp16 operand, fp32 accumulator; 4-6% faster there, 2-4%
+  // slower at D = 64). Sums of the unrounded fp32 values cost the same but
+  // let a peaked row's O drift by the fp16 rounding of its dominant weight
+  // (3.7e-3 against 2.0e-3 at peaked causal B4 H32 S4096 D128).
+  static constexpr bool MIX_SUMS = D == 128;
   // A wave in its softmax raises its issue priority (s_setprio), so that the
   // SIMD's other wave, in its MFMA phase or later in its own softmax, does not
   // starve it (2-3% on every workload).
@@ -463,8 +467,8 @@ __device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
   // Left to itself at D = 128, the scheduler reads most fragments just
   // before their MFMAs (fewer live registers), so the phase waits on LDS
   // latency unit after unit and the other wave's softmax fills the gaps;
-  // pinned, the MFMAs issue back to back (with the fp32-add row sums 4-6%
-  // faster; with v_dot2 sums 2-5% slower, as their softmax then waits).
+  // pinned, the MFMAs issue back to back (with the mixed-precision row sums
+  // 4-6% faster; with v_dot2 sums 2-5% slower, as their softmax then waits).
   pin_reads<0, AHEAD, NPV>();
   pin_units<0, NU, NPV, AHEAD, QSUB>();
 }
@@ -558,6 +562,18 @@ __device__ __forceinline__ float exp2_poly(float x) {
   return __uint_as_float(__float_as_uint(p) + ((uint32_t)(int)fl << 23));
 }
 
+// acc + the low (high) fp16 half of hp, exactly converted, in one fp32
+// rounding: v_fma_mix_f32 with an fp16 first operand and 1.0, which the
+// compiler does not form from C on its own.
+__device__ __forceinline__ float add_f16_lo(float acc, uint32_t hp) {
+  asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(hp));
+  return acc;
+}
+__device__ __forceinline__ float add_f16_hi(float acc, uint32_t hp) {
+  asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(hp));
+  return acc;
+}
+
 // exp2(t - m) of a 4-score accumulator, hidden keys forced to 0 when MASK;
 // with POLY the last of the four on the FMA path.
 template <bool MASK, bool POLY>
@@ -624,8 +640,8 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
         }
       }
     }
-  // Row sums: dot products of the rounded probabilities with ones, or (with
-  // ADD_SUMS) fp32 adds of the unrounded ones. With SUM_ONTO_D (D = 64) a
+  // Row sums of the rounded probabilities: dot products with ones, or (with
+  // MIX_SUMS) one mixed-precision add per value. With SUM_ONTO_D (D = 64) a
   // sub-tile's sum is one chain started from the lane's denominator (dnew,
   // whose excess over d is the tile's sum); else two chains from zero
   // (tsum), added onto d afterwards. The tile's sum is tested against the
@@ -647,11 +663,12 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
         h[4 + r] = (_Float16)p[2 * kc + 1][r];
       }
       pf[qs][kc] = h;
-      if constexpr (G::ADD_SUMS) {
+      if constexpr (G::MIX_SUMS) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[0] += p[2 * kc][r];
-          acc[1] += p[2 * kc + 1][r];
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t hp = __builtin_bit_cast(uint32_t, f16x2{h[e], h[e + 1]});
+          acc[0] = add_f16_lo(acc[0], hp);
+          acc[1] = add_f16_hi(acc[1], hp);
         }
       } else {
 #pragma unroll
@@ -662,7 +679,7 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
         }
       }
     }
-    static_assert(!(SUM_ONTO_D && G::ADD_SUMS), "one fp32 chain per sub-tile with v_dot2 only");
+    static_assert(!(SUM_ONTO_D && G::MIX_SUMS), "one fp32 chain per sub-tile with v_dot2 only");
     if (SUM_ONTO_D)
       dnew[qs] = acc[0];
     else
