@@ -43,8 +43,9 @@
 // first step of a tile takes the max up front; later redos leave a headroom
 // of MAX_HEADROOM above it). Because o and d always share one m, the result is
 // the same softmax, and probabilities up to P_LIMIT keep fp16's relative
-// precision. The row sum adds the fp16-rounded probabilities (v_dot2), so d
-// normalises exactly the weights the P.V product used.
+// precision. The row sum adds the fp16-rounded probabilities (v_dot2 at
+// D = 64, v_fma_mix_f32 at D = 128), so d normalises exactly the weights the
+// P.V product used.
 //
 // LDS. K and V tiles arrive by direct global->LDS loads into two-slot rings
 // of tile groups, one barrier interval before they are read. K rows are stored in
@@ -142,14 +143,15 @@ struct Geometry {
   static constexpr int SLOT_HALVES = NPH * K_HALVES;        // one interval's tiles
   // Q^T fragments stay in registers for the whole key loop at both head
   // dimensions. (At D = 128 they were staged in LDS and re-read each interval
-  // while the kernel needed 250 VGPRs; at 236 with them in registers it runs
-  // 1-2% faster and reads 64 KB less from LDS per interval and CU.)
+  // while the kernel needed 250 VGPRs; with them in registers it runs 1-2%
+  // faster and reads 64 KB less from LDS per interval and CU.)
   // The second wave of each SIMD (waves 4-7) runs half an interval out of
   // phase with the first (softmax against the other wave's MFMA phase). This
   // pays only where the MFMA phase is long next to the softmax: at D = 128
-  // (5% on causal B2 H16 S8192), not at D = 64 (2-10% slower, 3-4% with
-  // fp32-add row sums in place of the v_dot2 sums that wait for the other
-  // wave's MFMAs, and no better with the V operands in registers).
+  // (5% on causal B2 H16 S8192, 4-6% more with dense MFMA phases and row
+  // sums without v_dot2), not at D = 64 (2-10% slower, 3-4% with fp32-add
+  // row sums in place of the v_dot2 sums that wait for the other wave's
+  // MFMAs, and no better with the V operands in registers).
   static constexpr bool PINGPONG = D == 128 && (VAR & VAR_SYNC) == 0;
   // Synchronous copies (VAR_SYNC, a check of the ring protocol): each wave
   // waits for its copies and meets the others at a barrier right after
