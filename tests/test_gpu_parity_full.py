@@ -50,3 +50,21 @@ def test_non_causal_rounds_every_head_and_row(B, H, S, D):
     O, L = oracle_full(q, k, v, scale, False, workers=WORKERS)
     stats = compare(o, l, O, L, f"B{B}H{H}S{S}D{D}")
     print(f"[gpu-parity-full] B{B} H{H} S{S} D{D}: {stats}", flush=True)
+
+
+@pytest.mark.parametrize("B,H,S", [(1, 8, 4096), (1, 12, 4000)], ids=["H8S4096", "H12S4000"])
+def test_causal_three_waves_every_head_and_row(B, H, S):
+    """Causal single passes at D = 64 whose query tiles are not folded run
+    three waves per SIMD from 2048 keys (the diagonal falls in different
+    phases of a 192-key interval, and S = 4000 adds a key tail): every head
+    and row against the oracle."""
+    from testkit import make_qkv
+
+    D = 64
+    print(f"[gpu-parity-full] B{B} H{H} S{S} D{D} causal", flush=True)
+    q, k, v = make_qkv(B, H, S, D, 9800 + S)
+    scale = D ** -0.5
+    o, l = run_gpu(q, k, v, scale, True)
+    O, L = oracle_full(q, k, v, scale, True, workers=WORKERS)
+    stats = compare(o, l, O, L, f"B{B}H{H}S{S}D{D}c")
+    print(f"[gpu-parity-full] B{B} H{H} S{S} D{D} causal: {stats}", flush=True)
