@@ -86,3 +86,22 @@ def test_configs_are_the_five_problem_shapes():
     for n in CONFIGS:
         w = WORKLOADS[n]
         assert w.scale == float(np.float32(1.0 / np.sqrt(w.D)))
+
+
+def test_kernel_label_names_the_launched_instantiation():
+    """The roofline's kernel label follows the library's geometry choice:
+    three waves per SIMD (variant 128) at D = 64 from 2048 keys, folded causal
+    pairs from 8192; two waves below and at D = 128."""
+    import bench
+    from testkit import WORKLOADS
+
+    want = {
+        "listing_b1h4s128d64": "attn_fwd_kernel<64,false,false,0>",
+        "sdpa_b1h8s4096d64": "attn_fwd_kernel<64,false,false,128>",
+        "long_b1h8s16384d64": "attn_fwd_kernel<64,false,false,128>",
+        "causal_b2h16s8192d128": "attn_fwd_kernel<128,true,false,0>",
+        "peaked_causal_b4h32s4096d128": "attn_fwd_kernel<128,true,false,0>",
+        "sweep_causal_b1h8s4096d64": "attn_fwd_kernel<64,true,false,128>",
+    }
+    for name, label in want.items():
+        assert bench.kernel_label(WORKLOADS[name]) == label, name
