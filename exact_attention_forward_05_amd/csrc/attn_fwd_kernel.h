@@ -99,6 +99,7 @@ enum : int {
   VAR_PROD = 64,     // D = 64: four producer waves issue every K/V copy
   VAR_TRIO = 128,    // D = 64: three waves per SIMD over three 64-key tiles per interval
   VAR_QUAD = 256,    // D = 64: four waves per SIMD over four 32-key tiles per interval
+  VAR_ROT = 512,     // D = 64: three waves per SIMD, their phases rotated by a third
 };
 
 template <int D, int VAR = 0>
@@ -111,7 +112,13 @@ struct Geometry {
   // Three waves per SIMD (VAR_TRIO, D = 64): twelve compute waves, three per
   // query group, each on its own 64-key tile of a 192-key interval (three
   // 159-VGPR allocations fit a SIMD's 512 registers per lane).
-  static constexpr bool TRIO = D == 64 && (VAR & VAR_TRIO) != 0;
+  static constexpr bool TRIO = D == 64 && (VAR & (VAR_TRIO | VAR_ROT)) != 0;
+  // Rotated order (VAR_ROT, three-wave geometry): the three waves of a SIMD
+  // run P.V of interval j-1, Q.K^T of j and the softmax of j in the same
+  // order but with their barriers after different parts, so that at any
+  // time two of them issue MFMAs and one its softmax. Q.K^T of j runs in
+  // interval j for two waves and in j+1 for the third: a three-slot K ring.
+  static constexpr bool ROT = D == 64 && (VAR & VAR_ROT) != 0;
   // Four waves per SIMD (VAR_QUAD, D = 64): sixteen compute waves, four per
   // query group on 32-key tiles of a 128-key interval, at most 128 VGPRs.
   static constexpr bool QUAD = D == 64 && (VAR & VAR_QUAD) != 0;
@@ -139,6 +146,7 @@ struct Geometry {
   // barrier was waited for at this one.
   static constexpr bool BAR2 = D == 64 && (VAR & VAR_BAR2) != 0;
   static constexpr int RING = BAR2 ? 4 : (D == 64 && (VAR & VAR_RING3) != 0) ? 3 : 2;
+  static constexpr int KRING = ROT ? 3 : RING;  // slots of the K ring (V: RING)
   static constexpr int AHEAD = BAR2 ? 2 : RING - 1;  // intervals between a copy and its use
   static constexpr int SLOT_HALVES = NPH * K_HALVES;        // one interval's tiles
   // Q^T fragments stay in registers for the whole key loop at both head
@@ -162,7 +170,7 @@ struct Geometry {
   // softmax (three phases, V copied one interval earlier): the SIMD's two
   // waves then interleave shorter MFMA phases with their softmaxes (1-3%
   // faster). At D = 128 the ping-pong order measured faster than this.
-  static constexpr bool PV_SAME = D == 64;
+  static constexpr bool PV_SAME = D == 64 && !ROT;
   // Row sums of the rounded fp16 probabilities (the weights P.V uses, so that
   // a row dominated by one key gets exactly that key's V row). At D = 64,
   // dot products with ones (v_dot2). In the D = 128 ping-pong a softmax runs
@@ -208,7 +216,8 @@ struct Geometry {
   static_assert(LOADS * 64 * NCOP == PIECES, "tiling");
   static_assert(!PROD || VAR == VAR_PROD, "producer waves run the default two-slot ring alone");
   static_assert(!QUAD || VAR == VAR_QUAD, "four waves per SIMD run the default order alone");
-  static_assert(!TRIO || (VAR & ~VAR_SYNC) == VAR_TRIO,
+  static_assert(!ROT || VAR == VAR_ROT, "the rotated order runs alone");
+  static_assert(!TRIO || ROT || (VAR & ~VAR_SYNC) == VAR_TRIO,
                 "three waves per SIMD run the default order (or its synchronous-copy check)");
   static_assert(QSUB * 16 * QGROUPS == BLOCK_M && KB >= 2 && KC >= 1, "geometry");
   // Carrier hand-off (after the key loop): each wave finalises the output's
@@ -220,7 +229,7 @@ struct Geometry {
   static constexpr int MD_SLOTS = (QSUB + 1) / 2;
   static constexpr int HANDOFF_SLOTS = MD_SLOTS + QSUB * D_BLOCKS;
   static constexpr int HANDOFF_BYTES = CWAVES * HANDOFF_SLOTS * 64 * 16;
-  static constexpr int LOOP_BYTES = 2 * RING * SLOT_HALVES * 2;
+  static constexpr int LOOP_BYTES = (KRING + RING) * SLOT_HALVES * 2;
   static constexpr int LDS_BYTES = LOOP_BYTES > HANDOFF_BYTES ? LOOP_BYTES : HANDOFF_BYTES;
   static constexpr int LDS_HALVES = LDS_BYTES / 2;
   static_assert(D_BLOCKS >= NPH, "every wave of a query group owns an output block");
@@ -419,7 +428,7 @@ __device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
   constexpr int NPV = PV ? G::KC * G::D_BLOCKS : 0;
   constexpr int NQK = QK ? G::KB * G::D_CHUNKS : 0;
   constexpr int NU = NPV + NQK;
-  constexpr int AHEAD_MAX = G::QUAD ? 4 : D == 64 ? 8 : 4;
+  constexpr int AHEAD_MAX = (G::QUAD || G::ROT) ? 4 : D == 64 ? 8 : 4;
   constexpr int AHEAD = AHEAD_MAX < NU ? AHEAD_MAX : NU;
   // V^T operand (d block db, key chunk kc): lane (i, g) needs
   // V[32kc + 8g + e][16db + i], e = 0..7 -- two transposing reads over 4 key
@@ -786,7 +795,7 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
   constexpr int NPH = G::NPH;
   __shared__ __attribute__((aligned(16))) _Float16 smem[G::LDS_HALVES];
   _Float16* kring = smem;                           // [slot][tile] K tiles
-  _Float16* vring = smem + R * G::SLOT_HALVES;      // [slot][tile] V tiles
+  _Float16* vring = smem + G::KRING * G::SLOT_HALVES;  // [slot][tile] V tiles
 
   const int split = SPLIT ? (int)(blockIdx.x % (unsigned)n_splits) : 0;
   const int bid = SPLIT ? (int)(blockIdx.x / (unsigned)n_splits) : (int)blockIdx.x;
@@ -957,10 +966,12 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     // in interval j-1. Every wave runs all n_int + 1 intervals; the bodies
     // are specialised (compile-time flags) so that the steady state has no
     // branches.
+    // K ring slot of interval j (two slots, or three with ROT)
+    auto kslot_of = [](int j) { return G::KRING == 2 ? (j & 1) : (int)((unsigned)j % G::KRING); };
     auto copies = [&](int j) __attribute__((always_inline)) {
       if (j + 1 < n_int)
         copy_group<D, VAR>(cp.k_off, kh, pos(j + 1) * G::IKEYS, S,
-                      kring + ((j + 1) & 1) * G::SLOT_HALVES, cw);
+                      kring + kslot_of(j + 1) * G::SLOT_HALVES, cw);
       if (j < n_int)
         copy_group<D, VAR>(cp.v_off, vh, pos(j) * G::IKEYS, S,
                       vring + (j & 1) * G::SLOT_HALVES, cw);
@@ -982,7 +993,7 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     auto mfma = [&](int j, auto pv_flag, auto qk_flag) __attribute__((always_inline)) {
       constexpr bool PV = decltype(pv_flag)::value;
       constexpr bool QK = decltype(qk_flag)::value;
-      const _Float16* kslot = kring + (j & 1) * G::SLOT_HALVES + phase * G::K_HALVES;
+      const _Float16* kslot = kring + kslot_of(j) * G::SLOT_HALVES + phase * G::K_HALVES;
       const _Float16* vslot = vring + ((j + 1) & 1) * G::SLOT_HALVES + phase * G::V_HALVES;
       if constexpr (PV || QK) mfma_phase<D, VAR, PV, QK>(cr, pf, sc, qf, vslot, kslot, li, g);
     };
@@ -1159,8 +1170,44 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
       // the second after its softmax. Every wave runs n_int + 1 bodies, each
       // with one barrier.
       const bool second = PINGPONG && late;
+      // ROT: role r = wave / 4 (the r-th wave of each SIMD) ends its interval
+      // after the softmax (0), after Q.K^T (1) or after P.V (2), and issues
+      // the copies of an interval right after the barrier that opens it.
+      // Interval k then holds, per role: P.V of k-1, Q.K^T of k, softmax of
+      // k (0); softmax of k-1, P.V of k-1, Q.K^T of k (1); Q.K^T of k-1,
+      // softmax of k-1, P.V of k-1 (2). K of k-1 and k are read in interval
+      // k (a three-slot K ring), V of k-1 only; the copies of interval k
+      // (K of k+1, V of k) overwrite K of k-2 and V of k-2, last read in
+      // interval k-1.
+      const int role = G::ROT ? wave / (G::CWAVES / 3) : 0;
+      auto end_interval_rot = [&](int jj) __attribute__((always_inline)) {
+        wait_copies();
+        __syncthreads();
+        copies(jj + 1);
+      };
       auto body = [&](int jj, auto pv_flag, auto qk_flag, auto edge_flag) __attribute__((always_inline)) {
+        constexpr bool PV = decltype(pv_flag)::value;
         constexpr bool QK = decltype(qk_flag)::value;
+        if constexpr (G::ROT) {
+          if (role == 0) copies(jj);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma(jj, pv_flag, F_{});
+          __builtin_amdgcn_sched_barrier(0);
+          if (role == 2) end_interval_rot(jj);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma(jj, F_{}, qk_flag);
+          __builtin_amdgcn_sched_barrier(0);
+          if (role == 1) end_interval_rot(jj);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (QK) softmax_int(jj, edge_flag);
+          __builtin_amdgcn_sched_barrier(0);
+          if (role == 0) {
+            wait_copies();
+            __syncthreads();
+          }
+          (void)PV;
+          return;
+        }
         mfma(jj, pv_flag, qk_flag);
         __builtin_amdgcn_sched_barrier(0);
         if (second) {
@@ -1179,7 +1226,7 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
           __syncthreads();
         }
       };
-      if (second) copies(0);
+      if (second || (G::ROT && role != 0)) copies(0);
       if (n_live >= 1)
         body(j++, F_{}, T_{}, T_{});
       else

@@ -133,6 +133,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                                  /* over 192-key intervals                       */
 #define ATTN_VARIANT_QUAD 256    /* D = 64: sixteen compute waves, four per SIMD, */
                                  /* on 32-key tiles                              */
+#define ATTN_VARIANT_ROT 512     /* D = 64: three waves per SIMD whose phases are */
+                                 /* rotated by a third of an interval            */
 
 /*
  * attn_fwd_variant -- attn_fwd with a chosen compiled variant of the kernel,
@@ -168,6 +170,12 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *    variant runs it for any shape, for comparison.
  *  - ATTN_VARIANT_QUAD: four compute waves per SIMD (sixteen per workgroup,
  *    four 32-key tiles per 128-key interval, at most 128 VGPRs per wave).
+ *  - ATTN_VARIANT_ROT: the three-wave geometry with the waves of each SIMD
+ *    a third of an interval apart (P.V of the previous tile, Q.K^T and the
+ *    softmax of the current one, each wave meeting the barrier after a
+ *    different one of the three), so that two waves issue MFMAs while the
+ *    third runs its softmax (Part 2, Refused Optimizations: ping-pong
+ *    scheduling of two consumer warpgroups, here with three).
  *  - ATTN_VARIANT_SYNC: a check of the K/V ring protocol rather than an
  *    optimisation: every copy into LDS is waited for and followed by a
  *    workgroup barrier right after it is issued (and D = 128 runs lock-step,
@@ -177,7 +185,7 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *
  *  q ... causal, stream : as attn_fwd (same layouts, checks and status codes).
  *  variant : one of the ATTN_VARIANT_* values; D = 64 builds 0, RING3,
- *            EXP_POLY, WIDE, SUBPIPE, SYNC, BAR2, PROD, TRIO and QUAD,
+ *            EXP_POLY, WIDE, SUBPIPE, SYNC, BAR2, PROD, TRIO, QUAD and ROT,
  *            D = 128 builds 0, EXP_POLY and SYNC. Any other
  *            value (or combination) returns ATTN_ERR_UNSUPPORTED before
  *            anything is enqueued.

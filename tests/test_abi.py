@@ -196,7 +196,9 @@ VARIANT_REFUSED = [
     ("D128 wide", dict(D=128, variant=4), "ATTN_ERR_UNSUPPORTED"),
     ("combined flags", dict(variant=3), "ATTN_ERR_UNSUPPORTED"),
     ("D128 subpipe", dict(D=128, variant=8), "ATTN_ERR_UNSUPPORTED"),
-    ("unknown flag", dict(variant=512), "ATTN_ERR_UNSUPPORTED"),
+    ("unknown flag", dict(variant=1024), "ATTN_ERR_UNSUPPORTED"),
+    ("D128 rotated", dict(D=128, variant=512), "ATTN_ERR_UNSUPPORTED"),
+    ("rotated with three waves", dict(variant=640), "ATTN_ERR_UNSUPPORTED"),
     ("D128 quad", dict(D=128, variant=256), "ATTN_ERR_UNSUPPORTED"),
     ("D128 trio", dict(D=128, variant=128), "ATTN_ERR_UNSUPPORTED"),
     ("D128 producers", dict(D=128, variant=64), "ATTN_ERR_UNSUPPORTED"),
