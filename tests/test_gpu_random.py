@@ -51,3 +51,27 @@ def test_random_shape(case):
     os_, ls_ = attn.fwd_splitkv(qt, kt, vt, n_splits=n_splits, scale=scale, causal=causal)
     torch.cuda.synchronize()
     compare(os_.cpu().numpy(), ls_.cpu().numpy(), O, L, f"split-KV {case}")
+
+
+def _long_cases(n=8, seed=20261203):
+    """D = 64 shapes from 2048 keys with ragged lengths, both masks: the
+    three-wave geometry (192-key intervals, tails in any of the three
+    phases) for the single pass; split runs keep two waves when causal."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        S = int(rng.integers(2048, 9000))
+        H = int(rng.integers(1, 3))
+        causal = bool(i % 2)
+        scale = float(np.float32(0.125)) if rng.random() < 0.5 else float(
+            np.float32(rng.uniform(-0.5, 0.5)))
+        mult = float(rng.choice([1.0, 3.0]))
+        n_splits = int(rng.integers(1, 5))
+        out.append((1, H, S, 64, causal, scale, mult, n_splits, 2000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _long_cases(), ids=lambda c: "B{}H{}S{}D{}{}s{:.3f}x{}n{}".format(
+    c[0], c[1], c[2], c[3], "c" if c[4] else "n", c[5], c[6], c[7]))
+def test_random_long_shape(case):
+    test_random_shape(case)
