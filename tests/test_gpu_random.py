@@ -54,9 +54,11 @@ def test_random_shape(case):
 
 
 def _long_cases(n=8, seed=20261203):
-    """D = 64 shapes from 2048 keys with ragged lengths, both masks: the
-    three-wave geometry (192-key intervals, tails in any of the three
-    phases) for the single pass; split runs keep two waves when causal."""
+    """Shapes from 2048 keys with ragged lengths, both masks and random
+    scales: at D = 64 the three-wave geometry (192-key intervals, tails in
+    any of the three phases; split runs keep two waves when causal), at
+    D = 128 the ping-pong order; long rows whose max keeps climbing exercise
+    the lazy-max redo."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -68,6 +70,15 @@ def _long_cases(n=8, seed=20261203):
         mult = float(rng.choice([1.0, 3.0]))
         n_splits = int(rng.integers(1, 5))
         out.append((1, H, S, 64, causal, scale, mult, n_splits, 2000 + i))
+    rng = np.random.default_rng(seed + 1)
+    for i in range(n // 2 + 2):
+        S = int(rng.integers(2048, 6000))
+        causal = bool(i % 2)
+        scale = float(np.float32(128 ** -0.5)) if rng.random() < 0.5 else float(
+            np.float32(rng.uniform(-0.4, 0.4)))
+        mult = float(rng.choice([1.0, 3.0]))
+        n_splits = int(rng.integers(1, 5))
+        out.append((1, int(rng.integers(1, 3)), S, 128, causal, scale, mult, n_splits, 2100 + i))
     return out
 
 
