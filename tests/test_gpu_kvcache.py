@@ -76,6 +76,17 @@ def test_kvcache_peaked_scores():
     compare(o, l, O, L, "peaked kvcache")
 
 
+@pytest.mark.parametrize("scale,causal,ns", [(1.0, True, "auto"), (-0.5, False, 16), (2.0, True, 5)],
+                         ids=["s1c", "s-0.5n", "s2c"])
+def test_kvcache_large_scales(scale, causal, ns):
+    """Long caches with scales far above 1/sqrt(D): rows dominated by a few
+    keys, redos of the running max in most runs, split runs merged."""
+    q, k, v = _cache_inputs(1, 4, 16, 40000, 64, 9470 + int(4 * scale))
+    o, l = _run(q, k, v, scale, causal, ns)
+    O, L = oracle_full(q, k, v, scale, causal, row_chunk=64)
+    print(f"[gpu-kvcache] scale {scale}: {compare(o, l, O, L, f'large scale {scale}')}", flush=True)
+
+
 def test_decode_row_is_last_row_of_square_problem():
     """One causal query against the cache equals the last row of the square
     causal problem whose last query it is (the bottom-right alignment)."""
