@@ -55,6 +55,12 @@ CASES = [
     # (the cases above take a wave per row)
     (1, 4, 1100, 64, True, 0.125, 3, 10),
     (1, 2, 1100, 128, False, 0.08838834764831845, 2, 11),
+    # from 2048 keys the non-causal D = 64 runs take three waves per SIMD
+    # (192-key intervals): ragged tails, uneven runs, peaked and negative scales
+    (1, 2, 2500, 64, False, 0.125, 2, 12),
+    (1, 1, 3001, 64, False, 0.125, 3, 13),
+    (1, 2, 2048, 64, False, 1.0, 4, 14),     # peaked rows: frequent max redos per run
+    (1, 1, 2113, 64, False, -0.5, 5, 15),
 ]
 
 
@@ -67,12 +73,17 @@ def test_splitkv_small_full_compare(case):
     o, l = run_split(q, k, v, scale, causal, n_splits, ws_fill=0xFF)  # NaN-filled workspace
     O, L = oracle.sdpa_forward(q, k, v, scale, causal)
     compare(o, l, O, L, f"splitkv {case}")
-    # Against the single-pass path: each run rounds its probabilities to fp16
-    # relative to its own running max, so the two denominators differ by up
-    # to about 2^-12 relative (peaked rows) and LSE by as much.
+    # Against the single-pass path. Each path rounds every probability to fp16
+    # (relative error at most 2^-11) against its own running maximum, which
+    # the lazy rescale lets lag the true one, so the dominant terms of a
+    # peaked row need not be exactly 1: either denominator may sit up to
+    # 2^-11 relative from the exact sum, the two in opposite directions, and
+    # LSE (the log of the denominator) differs by up to 2^-10 = 9.8e-4. O
+    # divides by the same rounded sum it weights with, so its error stays
+    # at the fp16 output rounding.
     o1, l1 = run_gpu(q, k, v, scale, causal)
     assert np.abs(o.astype(np.float64) - o1).max() <= 2e-3
-    assert np.abs(l.astype(np.float64) - l1).max() <= 5e-4
+    assert np.abs(l.astype(np.float64) - l1).max() <= 1e-3
 
 
 def test_one_split_is_the_single_pass_path_bitwise():
@@ -103,14 +114,18 @@ def test_splitkv_workload_sampled_rows(name, n_splits):
         compare(o[b, h, rows], l[b, h, rows], O, L, f"{name} b{b} h{h}")
 
 
-def test_workspace_and_outputs_stay_in_bounds():
+@pytest.mark.parametrize("S,D,causal", [(500, 128, True), (2300, 64, False)],
+                         ids=["two_waves_d128_causal", "three_waves_d64"])
+def test_workspace_and_outputs_stay_in_bounds(S, D, causal):
     """Workspace and outputs inside larger canary-filled buffers, raw C entry
     point on a non-default stream."""
     import torch
 
     from exact_attention_forward_05_amd import _lib
 
-    B, H, S, D, ns = 1, 2, 500, 128, 3
+    B, H, ns = 1, 2, 3
+    scale = float(1.0 / np.sqrt(D))
+    _announce(f"canary S={S} D={D} causal={causal}")
     q, k, v = make_qkv(B, H, S, D, 9602)
     dev = torch.device("cuda:0")
     qt, kt, vt = (torch.from_numpy(x).to(dev) for x in (q, k, v))
@@ -125,7 +140,7 @@ def test_workspace_and_outputs_stay_in_bounds():
     with torch.cuda.stream(st):
         rc = _lib.attn_fwd_splitkv(qt.data_ptr(), kt.data_ptr(), vt.data_ptr(),
                                    obuf.data_ptr() + 2 * guard, lbuf.data_ptr() + 4 * guard,
-                                   B, H, S, D, 0.08838834764831845, 1, ns,
+                                   B, H, S, D, scale, int(causal), ns,
                                    wbuf.data_ptr() + guard, need, st.cuda_stream)
     _lib.check(rc)
     st.synchronize()
@@ -134,6 +149,6 @@ def test_workspace_and_outputs_stay_in_bounds():
     ob, lb = obuf.cpu().numpy(), lbuf.cpu().numpy()
     assert (ob[:guard] == -7.0).all() and (ob[guard + n:] == -7.0).all()
     assert (lb[:guard] == -7.0).all() and (lb[guard + B * H * S:] == -7.0).all()
-    O, L = oracle.sdpa_forward(q, k, v, 0.08838834764831845, True)
+    O, L = oracle.sdpa_forward(q, k, v, scale, causal)
     compare(ob[guard:guard + n].reshape(B, H, S, D), lb[guard:guard + B * H * S].reshape(B, H, S),
             O, L, "splitkv canary")
