@@ -367,9 +367,10 @@ VARIANT_BENCH = (("sdpa_b1h8s4096d64", 1), ("sdpa_b1h8s4096d64", 2), ("sdpa_b1h8
                  ("long_b1h8s16384d64", 32), ("sdpa_b1h8s4096d64", 64),
                  ("long_b1h8s16384d64", 64), ("sdpa_b1h8s4096d64", 256),
                  ("sdpa_b1h8s4096d64", 512), ("long_b1h8s16384d64", 512),
+                 ("sdpa_b1h8s4096d64", 1152), ("long_b1h8s16384d64", 1152),
                  ("causal_b2h16s8192d128", 2))
 VARIANT_NAMES = {1: "ring3", 2: "exp_poly", 4: "wide", 8: "subpipe", 32: "bar2", 64: "prod",
-                 128: "trio", 256: "quad", 512: "rot"}
+                 128: "trio", 256: "quad", 512: "rot", 1024: "m32", 1152: "m32_trio"}
 
 
 def run_variants(attn, dev, stream, steps, prewarm_ms):

@@ -97,7 +97,8 @@ VARIANT_DEFAULT, VARIANT_RING3, VARIANT_EXP_POLY, VARIANT_WIDE = 0, 1, 2, 4
 VARIANT_SUBPIPE, VARIANT_SYNC, VARIANT_BAR2, VARIANT_PROD, VARIANT_TRIO = 8, 16, 32, 64, 128
 VARIANT_QUAD = 256
 VARIANT_ROT = 512
-VARIANTS = {64: (0, 1, 2, 4, 8, 16, 32, 64, 128, 256, 512), 128: (0, 2, 16)}
+VARIANT_M32 = 1024
+VARIANTS = {64: (0, 1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 1152), 128: (0, 2, 16)}
 
 
 def attn_fwd_variant(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,

@@ -20,7 +20,8 @@ static_assert(attn::VAR_RING3 == ATTN_VARIANT_RING3 && attn::VAR_EXP_POLY == ATT
                   attn::VAR_WIDE == ATTN_VARIANT_WIDE && attn::VAR_SUBPIPE == ATTN_VARIANT_SUBPIPE &&
                   attn::VAR_SYNC == ATTN_VARIANT_SYNC && attn::VAR_BAR2 == ATTN_VARIANT_BAR2 &&
                   attn::VAR_PROD == ATTN_VARIANT_PROD && attn::VAR_TRIO == ATTN_VARIANT_TRIO &&
-                  attn::VAR_QUAD == ATTN_VARIANT_QUAD && attn::VAR_ROT == ATTN_VARIANT_ROT,
+                  attn::VAR_QUAD == ATTN_VARIANT_QUAD && attn::VAR_ROT == ATTN_VARIANT_ROT &&
+                  attn::VAR_M32 == ATTN_VARIANT_M32,
               "variant flags of the kernel and of the header");
 
 namespace {
@@ -143,6 +144,9 @@ int dispatch_variant(const void* q, const void* k, const void* v, void* o, float
       case VAR_TRIO: return launch_variant<64, VAR_TRIO>(q, k, v, o, lse, B, H, S, scale, causal, st);
       case VAR_QUAD: return launch_variant<64, VAR_QUAD>(q, k, v, o, lse, B, H, S, scale, causal, st);
       case VAR_ROT: return launch_variant<64, VAR_ROT>(q, k, v, o, lse, B, H, S, scale, causal, st);
+      case VAR_M32: return launch_variant<64, VAR_M32>(q, k, v, o, lse, B, H, S, scale, causal, st);
+      case VAR_M32 | VAR_TRIO:
+        return launch_variant<64, VAR_M32 | VAR_TRIO>(q, k, v, o, lse, B, H, S, scale, causal, st);
       default: break;
     }
   } else {
@@ -155,10 +159,11 @@ int dispatch_variant(const void* q, const void* k, const void* v, void* o, float
   }
   return attn::plan::fail(msg(), ATTN_ERR_UNSUPPORTED,
                           "kernel variant %d is not built for D=%d (D=64: 0, %d, %d, %d, %d, %d, %d, %d, %d, "
-                          "%d, %d; D=128: 0, %d, %d)", variant, D, ATTN_VARIANT_RING3,
+                          "%d, %d, %d, %d; D=128: 0, %d, %d)", variant, D, ATTN_VARIANT_RING3,
                           ATTN_VARIANT_EXP_POLY, ATTN_VARIANT_WIDE, ATTN_VARIANT_SUBPIPE,
                           ATTN_VARIANT_SYNC, ATTN_VARIANT_BAR2, ATTN_VARIANT_PROD, ATTN_VARIANT_TRIO,
-                          ATTN_VARIANT_QUAD, ATTN_VARIANT_ROT, ATTN_VARIANT_EXP_POLY,
+                          ATTN_VARIANT_QUAD, ATTN_VARIANT_ROT, ATTN_VARIANT_M32,
+                          ATTN_VARIANT_M32 | ATTN_VARIANT_TRIO, ATTN_VARIANT_EXP_POLY,
                           ATTN_VARIANT_SYNC);
 }
 

@@ -67,6 +67,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BLOCK_M = 128;          // query rows per workgroup
@@ -100,6 +101,7 @@ enum : int {
   VAR_TRIO = 128,    // D = 64: three waves per SIMD over three 64-key tiles per interval
   VAR_QUAD = 256,    // D = 64: four waves per SIMD over four 32-key tiles per interval
   VAR_ROT = 512,     // D = 64: three waves per SIMD, their phases rotated by a third
+  VAR_M32 = 1024,    // D = 64: 32x32x16 MFMAs (one 32-row block per wave)
 };
 
 template <int D, int VAR = 0>
@@ -122,18 +124,30 @@ struct Geometry {
   // Four waves per SIMD (VAR_QUAD, D = 64): sixteen compute waves, four per
   // query group on 32-key tiles of a 128-key interval, at most 128 VGPRs.
   static constexpr bool QUAD = D == 64 && (VAR & VAR_QUAD) != 0;
+  // 32x32x16 MFMAs (VAR_M32, D = 64, 32-row waves): each wave's 32 query
+  // rows are one MFMA block. An MFMA takes one issue slot per 32 cycles
+  // instead of one per 16, so the softmax of another wave on the SIMD keeps
+  // more of its VALU rate beside it, and each K or V^T fragment read from
+  // LDS feeds 32 query columns. Measured: about 3% fewer cycles per launch,
+  // but under sustained load the power-limited clock drops from 2.1 to
+  // 1.9 GHz (twice the accumulator traffic per FLOP), 7% slower -- a
+  // variant. Lane (j, h) = (lane % 32, lane / 32) holds
+  // query j: of a 32-key block of S^T, keys 8e' + 4h + r (element 4e' + r);
+  // of O^T, rows 8e' + 4h + r of each 32-row block.
+  static constexpr bool M32 = D == 64 && (VAR & VAR_M32) != 0;
   static constexpr int NPH = (WIDE || QUAD) ? 4 : TRIO ? 3 : 2;
   static constexpr int CWAVES = TRIO ? 12 : QUAD ? 16 : WAVES;  // compute waves
   static constexpr int QGROUPS = CWAVES / NPH;             // query groups
   static constexpr int ROWS = BLOCK_M / QGROUPS;           // query rows per wave
-  static constexpr int QSUB = ROWS / 16;                   // 16-row query sub-tiles per wave
+  // 16-row query sub-tiles per wave (M32: the wave's one 32-row block)
+  static constexpr int QSUB = M32 ? 1 : ROWS / 16;
   // Keys per tile: each wave folds one tile per barrier interval. (At D = 64,
   // 64-row waves with 64-key tiles would not fit the 256-register budget of
   // two waves per SIMD; nor would 128-key tiles with 32-row waves.)
   static constexpr int BN = TRIO ? 64 : INTERVAL_KEYS / NPH;
   static constexpr int IKEYS = NPH * BN;                   // keys per barrier interval
-  static constexpr int KB = BN / 16;                       // 16-key MFMA blocks of S^T
-  static constexpr int KC = BN / 32;                       // 32-key chunks of the P.V contraction
+  static constexpr int KB = BN / (M32 ? 32 : 16);          // MFMA key blocks of S^T
+  static constexpr int KC = BN / (M32 ? 16 : 32);          // key chunks of the P.V contraction
   static constexpr int K_HALVES = BN * D;                  // K rows unpadded, swizzled
   static constexpr int V_HALVES = BN * D;                  // V rows unpadded, swizzled
   // Two-slot rings of tile groups (one tile per phase) for K and for V: one
@@ -198,8 +212,9 @@ struct Geometry {
   // of 3, 6, 10 and 16; fp32-add row sums in place of v_dot2 did not help).
   static constexpr bool SUBPIPE = D == 64 && (VAR & VAR_SUBPIPE) != 0 && QSUB == 2;
   static constexpr int SIDE_VPER = 3;
-  static constexpr int D_CHUNKS = D / 32;                  // contraction chunks of Q.K
-  static constexpr int D_BLOCKS = D / 16;                  // 16-row blocks of O^T
+  static constexpr int D_CHUNKS = D / (M32 ? 16 : 32);     // contraction chunks of Q.K
+  static constexpr int D_BLOCKS = D / (M32 ? 32 : 16);     // MFMA row blocks of O^T
+  using Acc = std::conditional_t<M32, f32x16, f32x4>;     // one MFMA accumulator
   // Producer waves (VAR_PROD, D = 64): the workgroup gets four more waves,
   // one per SIMD, that issue all K/V copies and only wait and synchronise;
   // the eight compute waves never touch global memory inside the key loop.
@@ -217,22 +232,31 @@ struct Geometry {
   static_assert(!PROD || VAR == VAR_PROD, "producer waves run the default two-slot ring alone");
   static_assert(!QUAD || VAR == VAR_QUAD, "four waves per SIMD run the default order alone");
   static_assert(!ROT || VAR == VAR_ROT, "the rotated order runs alone");
-  static_assert(!TRIO || ROT || (VAR & ~VAR_SYNC) == VAR_TRIO,
+  static_assert(!TRIO || ROT || (VAR & ~(VAR_SYNC | VAR_M32)) == VAR_TRIO,
                 "three waves per SIMD run the default order (or its synchronous-copy check)");
-  static_assert(QSUB * 16 * QGROUPS == BLOCK_M && KB >= 2 && KC >= 1, "geometry");
+  static_assert(!M32 || (VAR & ~(VAR_SYNC | VAR_TRIO)) == VAR_M32,
+                "32x32 MFMAs run the default two- or three-wave order (or its synchronous-copy check)");
+  static_assert(!M32 || ROWS == 32, "32x32 MFMAs need 32-row waves");
+  static_assert(ROWS * QGROUPS == BLOCK_M && (M32 || QSUB * 16 == ROWS) && KB >= 2 && KC >= 1,
+                "geometry");
   // Carrier hand-off (after the key loop): each wave finalises the output's
   // 16-column blocks it owns (block db belongs to phase db * NPH / D_BLOCKS:
   // an equal share, or at NPH = 3 blocks {0, 1}, {2}, {3}) for its rows. Per
   // wave, 16-byte slots of 64 lanes: {m, d} of two sub-tiles per slot, then
   // one slot per sub-tile and output block.
+  // (M32: the unit is a quarter block -- four accumulator elements, rows
+  // 8e' + 4h + r of block db for e' = quarter -- owned by phase
+  // quarter * NPH / (4 * D_BLOCKS).)
   static constexpr int owner(int db) { return db * NPH / D_BLOCKS; }
+  static constexpr int QUARTERS = 4 * D_BLOCKS;
+  static constexpr int owner_q(int qd) { return qd * NPH / QUARTERS; }
   static constexpr int MD_SLOTS = (QSUB + 1) / 2;
-  static constexpr int HANDOFF_SLOTS = MD_SLOTS + QSUB * D_BLOCKS;
+  static constexpr int HANDOFF_SLOTS = MD_SLOTS + (M32 ? QUARTERS : QSUB * D_BLOCKS);
   static constexpr int HANDOFF_BYTES = CWAVES * HANDOFF_SLOTS * 64 * 16;
   static constexpr int LOOP_BYTES = (KRING + RING) * SLOT_HALVES * 2;
   static constexpr int LDS_BYTES = LOOP_BYTES > HANDOFF_BYTES ? LOOP_BYTES : HANDOFF_BYTES;
   static constexpr int LDS_HALVES = LDS_BYTES / 2;
-  static_assert(D_BLOCKS >= NPH, "every wave of a query group owns an output block");
+  static_assert((M32 ? QUARTERS : D_BLOCKS) >= NPH, "every wave of a query group owns an output block");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -289,6 +313,12 @@ __device__ __forceinline__ int v_swizzle(int r) {
   return 2 * ((r & 3) + 4 * ((r >> 3) & 1));
 }
 
+// V with 32x32 MFMAs (M32, D = 64): each half-wave's transposing reads cover 4
+// consecutive key rows x 64 bytes; rows 2r and 2r + 1 fall on the two halves
+// of the 64 banks, and this swizzle puts rows 4r and 4r + 2 on disjoint
+// 64-byte groups of chunks.
+__device__ __forceinline__ int v_swizzle_m32(int r) { return 4 * ((r >> 1) & 1); }
+
 // Direct global->LDS copy of one interval's tiles. A buffer load with the LDS
 // flag writes lane l's 16 bytes at M0 + 16*l, so each wave instruction fills
 // 1 KB of LDS in slot order; each lane therefore fetches the global piece that
@@ -318,9 +348,11 @@ __device__ __forceinline__ void make_copy_plan(CopyPlan<D, VAR>& cp, int cw, int
     const int w = slot % TILE_SLOTS;
     const int row = w / CHUNKS;
     const int pc = w % CHUNKS;                       // physical chunk in the row
-    const int kkey = st_key(row >> 4, row & 15);
+    // (M32: K rows in key order, as the 32x32 operand reads them)
+    const int kkey = G::M32 ? row : st_key(row >> 4, row & 15);
+    const int vsw = G::M32 ? v_swizzle_m32(row) : v_swizzle<D>(row);
     cp.k_off[i] = (uint32_t)(((t * G::BN + kkey) * D + 8 * (pc ^ k_swizzle<D>(row))) * 2);
-    cp.v_off[i] = (uint32_t)(((t * G::BN + row) * D + 8 * (pc ^ v_swizzle<D>(row))) * 2);
+    cp.v_off[i] = (uint32_t)(((t * G::BN + row) * D + 8 * (pc ^ vsw)) * 2);
   }
 }
 
@@ -367,10 +399,12 @@ __device__ __forceinline__ f16x4 lds_read_tr(const _Float16* p) {
   return __builtin_bit_cast(f16x4, r);
 }
 
-// Per-lane carrier of one query sub-tile (the lane's query is i = lane % 16).
-template <int D>
+// Per-lane carrier of one query sub-tile (the lane's query is i = lane % 16;
+// M32: j = lane % 32).
+template <int D, int VAR>
 struct Carrier {
-  f32x4 o[Geometry<D>::D_BLOCKS];  // O^T rows 16*db + 4*g + r of this query
+  typename Geometry<D, VAR>::Acc o[Geometry<D, VAR>::D_BLOCKS];  // O^T rows of this query:
+                                   // 16*db + 4*g + r (M32: 32*db + 8e' + 4h + r)
   float m;                         // running max of t = s*c (base-2 units)
   float d;                         // this lane's share of the denominator
 };
@@ -378,11 +412,12 @@ struct Carrier {
 // Per-wave register sets: carriers and Q^T fragments of the QSUB sub-tiles, a
 // tile's scores, and its fp16 probabilities.
 template <int D, int VAR>
-using CarrierSet = Carrier<D>[Geometry<D, VAR>::QSUB];
+using CarrierSet = Carrier<D, VAR>[Geometry<D, VAR>::QSUB];
 template <int D, int VAR>
 using QSet = f16x8[Geometry<D, VAR>::QSUB][Geometry<D, VAR>::D_CHUNKS];
 template <int D, int VAR>
-using ScoreSet = f32x4[Geometry<D, VAR>::QSUB][Geometry<D, VAR>::KB];
+using ScoreSet = std::conditional_t<Geometry<D, VAR>::M32, f32x16[Geometry<D, VAR>::KB],
+                                    f32x4[Geometry<D, VAR>::QSUB][Geometry<D, VAR>::KB]>;
 template <int D, int VAR>
 using ProbSet = f16x8[Geometry<D, VAR>::QSUB][Geometry<D, VAR>::KC];
 
@@ -409,6 +444,67 @@ __device__ __forceinline__ void pin_units() {
   }
 }
 
+// The MFMA half of an interval with 32x32x16 MFMAs (M32): units as in
+// mfma_phase below, one MFMA each.
+//  V^T operand (O^T block ob, key chunk cc of 16 keys): lane (i, h) needs
+//  V[16cc + 4h + 8x + e][32ob + i] for x = 0, 1 and e = 0..3 -- the keys whose
+//  probabilities the lane holds in element 8(cc % 2) + 4x + e of the scores
+//  of block cc / 2 -- two transposing reads over 4 key rows x 16 d, source
+//  lane n of group g pointing at row 16cc + 4h + 8x + n/4, halves
+//  32ob + 16(g % 2) + 4(n % 4).
+//  K operand (key block kb, d chunk dc): row 32kb + i, halves 16dc + 8h.
+template <int D, int VAR, bool PV, bool QK>
+__device__ __forceinline__ void mfma_phase_m32(CarrierSet<D, VAR>& cr,
+                                               const ProbSet<D, VAR>& pf,
+                                               ScoreSet<D, VAR>& sc,
+                                               const QSet<D, VAR>& qf,
+                                               const _Float16* __restrict__ vtile,
+                                               const _Float16* __restrict__ ktile, int li, int g) {
+  using G = Geometry<D, VAR>;
+  constexpr int NPV = PV ? G::KC * G::D_BLOCKS : 0;
+  constexpr int NQK = QK ? G::KB * G::D_CHUNKS : 0;
+  constexpr int NU = NPV + NQK;
+  constexpr int AHEAD = 4 < NU ? 4 : NU;
+  const int i = 16 * (g & 1) + li;
+  const int h = g >> 1;
+  // row bit 1 (the swizzle's) is bit 3 of li, for every cc, h and x
+  const int vsw = v_swizzle_m32(li >> 2);
+  const _Float16* vlane = vtile + (4 * h + (li >> 2)) * D + 4 * (li & 1);
+  const int vx = 2 * (g & 1) + ((li & 3) >> 1);  // logical chunk within the block
+  const int ksw = k_swizzle<D>(i);  // the swizzle bits of row 32kb + i do not depend on kb
+  auto load = [&](int u) -> f16x8 {
+    if (u < NPV) {
+      const int cc = u / G::D_BLOCKS, ob = u % G::D_BLOCKS;
+      const _Float16* vp = vlane + 8 * ((4 * ob + vx) ^ vsw) + (16 * cc) * D;
+      const f16x4 lo = lds_read_tr(vp);
+      const f16x4 hi = lds_read_tr(vp + 8 * D);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const int w = u - NPV, dc = w / G::KB, kb = w % G::KB;
+    return *reinterpret_cast<const f16x8*>(ktile + (32 * kb + i) * D + 8 * ((2 * dc + h) ^ ksw));
+  };
+  auto compute = [&](int u, const f16x8& a) {
+    if (u < NPV) {
+      const int cc = u / G::D_BLOCKS, ob = u % G::D_BLOCKS;
+      cr[0].o[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[0][cc], cr[0].o[ob], 0, 0, 0);
+    } else {
+      const int w = u - NPV, dc = w / G::KB, kb = w % G::KB;
+      sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[0][dc], dc == 0 ? f32x16{} : sc[kb],
+                                                      0, 0, 0);
+    }
+  };
+  f16x8 fr[NU];
+#pragma unroll
+  for (int u = 0; u < AHEAD; ++u) fr[u] = load(u);
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (u + AHEAD < NU) fr[u + AHEAD] = load(u + AHEAD);
+    compute(u, fr[u]);
+  }
+  pin_reads<0, AHEAD, NPV>();
+  pin_units<0, NU, NPV, AHEAD, 1>();
+}
+
 // The MFMA half of an interval: P.V of the previous tile (PV) and Q.K^T of the
 // current one (QK), as one software-pipelined stream of units. A unit is one
 // A-operand fragment read from LDS (two transposing reads for V^T, one 16-byte
@@ -424,6 +520,9 @@ __device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
                                            const _Float16* __restrict__ vtile,
                                            const _Float16* __restrict__ ktile, int li, int g) {
   using G = Geometry<D, VAR>;
+  if constexpr (G::M32) {
+    mfma_phase_m32<D, VAR, PV, QK>(cr, pf, sc, qf, vtile, ktile, li, g);
+  } else {
   constexpr int QSUB = G::QSUB;
   constexpr int NPV = PV ? G::KC * G::D_BLOCKS : 0;
   constexpr int NQK = QK ? G::KB * G::D_CHUNKS : 0;
@@ -482,6 +581,7 @@ __device__ __forceinline__ void mfma_phase(CarrierSet<D, VAR>& cr,
   // 4-6% faster; with v_dot2 sums 2-5% slower, as their softmax then waits).
   pin_reads<0, AHEAD, NPV>();
   pin_units<0, NU, NPV, AHEAD, QSUB>();
+  }
 }
 
 // Operand fragments of one tile for the sub-tile pipelined interval
@@ -600,6 +700,82 @@ __device__ __forceinline__ f32x4 exp_block(f32x4 s, float c, float m, uint32_t h
   return p;
 }
 
+// Online softmax of one tile with 32x32 MFMAs (M32): the lane's 32 scores
+// of query j (element 4e' + r of block kb: key key0 + 32kb + 8e' + 4h + r),
+// probabilities packed in that order (chunk 2kb + x: elements 8x .. 8x + 7
+// of block kb), the row sum one v_dot2 chain started from the lane's share
+// of the denominator, and the lazy-max test and redo as in softmax_tile.
+// The two lanes of a query (h = 0, 1) meet by one lane swap.
+template <int D, int VAR, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void softmax_m32(CarrierSet<D, VAR>& cr, const ScoreSet<D, VAR>& sc,
+                                            ProbSet<D, VAR>& pf, float c, int key0, int qpos0,
+                                            int S, int li, int g, bool first) {
+  using G = Geometry<D, VAR>;
+  const int h = g >> 1;
+  uint32_t hid[G::KB];
+#pragma unroll
+  for (int kb = 0; kb < G::KB; ++kb) {
+    hid[kb] = 0u;
+    if (MASK) {
+      const int qpos = qpos0 + 16 * (g & 1) + li;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
+        const bool hd = key >= S || (CAUSAL && key > qpos);
+        hid[kb] |= (hd ? 1u : 0u) << e;
+      }
+    }
+  }
+  Carrier<D, VAR>& cw = cr[0];
+  float dnew = 0.0f;
+  auto expo = [&]() {
+    const float m = cw.m;
+    float acc = cw.d;
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        f16x8 hv;
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) {
+          const int e = 8 * x + e8;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][e], c, -m));
+          if (MASK) p = ((hid[kb] >> e) & 1u) ? 0.0f : p;
+          hv[e8] = (_Float16)p;
+        }
+        pf[0][2 * kb + x] = hv;
+#pragma unroll
+        for (int e8 = 0; e8 < 8; e8 += 2)
+          acc = __builtin_amdgcn_fdot2(f16x2{hv[e8], hv[e8 + 1]},
+                                       f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+      }
+    dnew = acc;
+  };
+  if (!first) expo();
+  const bool over = first || !(dnew <= cw.d + P_LIMIT);
+  if (__builtin_amdgcn_ballot_w64(over) != 0) {
+    float tmax = NEG_BIG;
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float sv = (MASK && ((hid[kb] >> e) & 1u)) ? NEG_BIG : sc[kb][e];
+        tmax = __builtin_fmaxf(tmax, sv);
+      }
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                              false, false);
+    tmax = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const float m_new = __builtin_fmaxf(cw.m, tmax * c);
+    const float alpha = __builtin_amdgcn_exp2f(cw.m - m_new);
+    cw.d *= alpha;
+#pragma unroll
+    for (int ob = 0; ob < G::D_BLOCKS; ++ob) cw.o[ob] *= alpha;
+    cw.m = m_new;
+    expo();
+  }
+  cw.d = dnew;
+}
+
 // Online softmax of one tile's scores: probabilities (fp16, P^T operand
 // layout) into pf, denominators and, when the max moves, outputs rescaled.
 struct NoSide {
@@ -630,6 +806,11 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
                                              int qpos0, int S, int li, int g, bool first,
                                              Side&& side = Side{}) {
   using G = Geometry<D, VAR>;
+  if constexpr (G::M32) {
+    static_assert(SIDE_MFMAS == 0 && QS_LO == 0, "32x32 MFMAs: whole-tile softmax only");
+    side();
+    softmax_m32<D, VAR, CAUSAL, MASK>(cr, sc, pf, c, key0, qpos0, S, li, g, first);
+  } else {
   constexpr int QSUB = QS_HI < 0 ? G::QSUB : QS_HI;  // one past the last sub-tile
   side();
   // hidden-key bits per sub-tile and key block (bit r: accumulator element
@@ -746,6 +927,7 @@ __device__ __forceinline__ void softmax_tile(CarrierSet<D, VAR>& cr,
   }
 #pragma unroll
   for (int qs = QS_LO; qs < QSUB; ++qs) cr[qs].d = SUM_ONTO_D ? dnew[qs] : cr[qs].d + tsum[qs];
+  }
 }
 
 template <int D, int VAR, bool CAUSAL, int QS_LO = 0, int QS_HI = -1, int SIDE_MFMAS = 0,
@@ -842,6 +1024,16 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     f16x8 qf[QSUB][G::D_CHUNKS];
     if (producer) {
       // no query rows
+    } else if constexpr (G::M32) {
+      // lane (j, h): row qrow0 + j, halves 16dc + 8h of each d chunk dc
+      const int row = qrow0 + 16 * (g & 1) + li;
+  #pragma unroll
+      for (int dc = 0; dc < G::D_CHUNKS; ++dc) {
+        u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+            qrs, ((uint32_t)row * D + 16u * dc + 8u * (g >> 1)) * 2u, 0, 0);
+        w ^= qsign;
+        qf[0][dc] = __builtin_bit_cast(f16x8, w);
+      }
     } else {
   #pragma unroll
       for (int qs = 0; qs < QSUB; ++qs) {
@@ -856,19 +1048,19 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
       }
     }
 
-    Carrier<D> cr[QSUB];
+    Carrier<D, VAR> cr[QSUB];
   #pragma unroll
     for (int qs = 0; qs < QSUB; ++qs) {
       cr[qs].m = NEG_BIG;
       cr[qs].d = 0.f;
   #pragma unroll
-      for (int db = 0; db < G::D_BLOCKS; ++db) cr[qs].o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db < G::D_BLOCKS; ++db) cr[qs].o[db] = typename G::Acc{};
     }
     // sc: a tile's scores between Q.K^T and softmax; pf: its fp16
     // probabilities between softmax and P.V (at D = 128 carried across the
     // barrier into the next interval).
-    f16x8 pf[QSUB][G::KC];
-    f32x4 sc[QSUB][G::KB];
+    ProbSet<D, VAR> pf;
+    ScoreSet<D, VAR> sc;
 
     const int kend = CAUSAL ? min(S, q0 + BLOCK_M + koff) : S;
     const int n_kt = (kend + G::BN - 1) / G::BN;
@@ -1237,6 +1429,82 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
       for (; j <= n_int; ++j) body(j, F_{}, F_{}, F_{});      // idle: copies, barriers
     }
 
+    float* lse_h = lse + (int64_t)bh * Sq;
+    _Float16* oh = o + qhead;
+    const int64_t part_row0 = ((int64_t)split * BH + bh) * Sq;  // SPLIT: workspace rows
+    f32x4* area = reinterpret_cast<f32x4*>(smem) + lane;
+    if constexpr (G::M32) {
+      // Carrier hand-off with 32x32 MFMAs: per wave one slot {m, d, -, -} and
+      // one slot per quarter block it does not finalise (quarter qd: elements
+      // 4(qd % 4) .. +3 of block qd / 4, O^T rows 32(qd / 4) + 8(qd % 4) + 4h
+      // + r); each wave merges the quarters it owns (owner_q(qd) == phase).
+      const int h = g >> 1;
+      auto md_slot = [&](int w) { return area + (w * G::HANDOFF_SLOTS) * 64; };
+      auto q_slot = [&](int w, int qd) {
+        return area + (w * G::HANDOFF_SLOTS + G::MD_SLOTS + qd) * 64;
+      };
+      auto quarter = [&](int qd) {
+        const f32x16& a = cr[0].o[qd / 4];
+        const int e0 = 4 * (qd % 4);
+        return f32x4{a[e0], a[e0 + 1], a[e0 + 2], a[e0 + 3]};
+      };
+      *md_slot(wave) = f32x4{cr[0].m, cr[0].d, 0.0f, 0.0f};
+  #pragma unroll
+      for (int qd = 0; qd < G::QUARTERS; ++qd)
+        if (G::owner_q(qd) != phase) *q_slot(wave, qd) = quarter(qd);
+      __syncthreads();
+      float mp[NPH], dp[NPH], w[NPH];
+      float m = NEG_BIG;
+  #pragma unroll
+      for (int p = 0; p < NPH; ++p) {
+        const f32x4 md = *md_slot(qgrp * NPH + p);
+        mp[p] = md[0];
+        dp[p] = md[1];
+        m = __builtin_fmaxf(m, mp[p]);
+      }
+      float dl = 0.0f;
+  #pragma unroll
+      for (int p = 0; p < NPH; ++p) {
+        w[p] = __builtin_amdgcn_exp2f(mp[p] - m);
+        dl += dp[p] * w[p];
+      }
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dl), __float_as_uint(dl), false,
+                                                 false);
+      const float dsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const int row = qrow0 + 16 * (g & 1) + li;
+      const bool empty = SPLIT && !(dsum > 0.0f);
+      const float inv = empty ? 0.0f : 1.0f / dsum;
+      if (row < Sq) {
+  #pragma unroll
+        for (int qd = 0; qd < G::QUARTERS; ++qd) {
+          if (G::owner_q(qd) != phase) continue;
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  #pragma unroll
+          for (int p = 0; p < NPH; ++p) {
+            if (p == G::owner_q(qd))
+              acc += quarter(qd) * w[p];
+            else
+              acc += *q_slot(qgrp * NPH + p, qd) * w[p];
+          }
+          const int col = 32 * (qd / 4) + 8 * (qd % 4) + 4 * h;
+          if constexpr (SPLIT) {
+            float* po = part_o + (part_row0 + row) * D;
+            *reinterpret_cast<f32x4*>(po + col) = acc * inv;
+          } else {
+            f16x4 hv;
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(acc[r] * inv);
+            *reinterpret_cast<f16x4*>(oh + (int64_t)row * D + col) = hv;
+          }
+        }
+        if (phase == 0 && h == 0) {
+          if constexpr (SPLIT)
+            part_lse[part_row0 + row] = empty ? NEG_BIG : m + log2f(dsum);
+          else
+            lse_h[row] = (m + log2f(dsum)) * 0.69314718055994530942f;
+        }
+      }
+    } else {
     // Carrier hand-off. Every wave leaves its carriers in LDS -- per pair of
     // sub-tiles one 16-byte slot {m, d, m, d}, and the output blocks it does
     // not finalise, one slot per block -- each lane at 16 * lane in a slot, so
@@ -1246,7 +1514,6 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
     // compile-time (unrolled loops with wave-uniform branches on the phase),
     // so no register array is indexed at run time. The last interval ended
     // with a barrier, so the ring is no longer read.
-    f32x4* area = reinterpret_cast<f32x4*>(smem) + lane;
     auto md_slot = [&](int w, int qs) { return area + (w * G::HANDOFF_SLOTS + qs / 2) * 64; };
     auto o_slot = [&](int w, int qs, int db) {
       return area + (w * G::HANDOFF_SLOTS + G::MD_SLOTS + qs * G::D_BLOCKS + db) * 64;
@@ -1267,9 +1534,6 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
         if (G::owner(db) != phase) *o_slot(wave, qs, db) = cr[qs].o[db];
     __syncthreads();
 
-    float* lse_h = lse + (int64_t)bh * Sq;
-    _Float16* oh = o + qhead;
-    const int64_t part_row0 = ((int64_t)split * BH + bh) * Sq;  // SPLIT: workspace rows
   #pragma unroll
     for (int qs = 0; qs < QSUB; ++qs) {
       // merged max, each carrier's weight, and the row's denominator
@@ -1324,6 +1588,7 @@ __global__ __launch_bounds__((Geometry<D, VAR>::WG_THREADS)) void attn_fwd_kerne
             lse_h[row] = (m + log2f(dsum)) * 0.69314718055994530942f;
         }
       }
+    }
     }
   };
   run_tile(work.qt_first);

@@ -135,6 +135,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                                  /* on 32-key tiles                              */
 #define ATTN_VARIANT_ROT 512     /* D = 64: three waves per SIMD whose phases are */
                                  /* rotated by a third of an interval            */
+#define ATTN_VARIANT_M32 1024    /* D = 64: 32x32x16 MFMAs; alone (two waves per  */
+                                 /* SIMD) or with ATTN_VARIANT_TRIO (three)      */
 
 /*
  * attn_fwd_variant -- attn_fwd with a chosen compiled variant of the kernel,
@@ -176,6 +178,10 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *    different one of the three), so that two waves issue MFMAs while the
  *    third runs its softmax (Part 2, Refused Optimizations: ping-pong
  *    scheduling of two consumer warpgroups, here with three).
+ *  - ATTN_VARIANT_M32: both products on 32x32x16 MFMAs, each wave's 32
+ *    query rows one MFMA block (the pages' kernels tile with the 5090's
+ *    16x8x16 mma.sync atoms; Part 2, Move 4). Alone with two waves per
+ *    SIMD, or with ATTN_VARIANT_TRIO (1152) with three.
  *  - ATTN_VARIANT_SYNC: a check of the K/V ring protocol rather than an
  *    optimisation: every copy into LDS is waited for and followed by a
  *    workgroup barrier right after it is issued (and D = 128 runs lock-step,

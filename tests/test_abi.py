@@ -196,7 +196,10 @@ VARIANT_REFUSED = [
     ("D128 wide", dict(D=128, variant=4), "ATTN_ERR_UNSUPPORTED"),
     ("combined flags", dict(variant=3), "ATTN_ERR_UNSUPPORTED"),
     ("D128 subpipe", dict(D=128, variant=8), "ATTN_ERR_UNSUPPORTED"),
-    ("unknown flag", dict(variant=1024), "ATTN_ERR_UNSUPPORTED"),
+    ("unknown flag", dict(variant=2048), "ATTN_ERR_UNSUPPORTED"),
+    ("D128 32x32 MFMAs", dict(D=128, variant=1024), "ATTN_ERR_UNSUPPORTED"),
+    ("32x32 MFMAs with a three-slot ring", dict(variant=1025), "ATTN_ERR_UNSUPPORTED"),
+    ("32x32 MFMAs rotated", dict(variant=1536), "ATTN_ERR_UNSUPPORTED"),
     ("D128 rotated", dict(D=128, variant=512), "ATTN_ERR_UNSUPPORTED"),
     ("rotated with three waves", dict(variant=640), "ATTN_ERR_UNSUPPORTED"),
     ("D128 quad", dict(D=128, variant=256), "ATTN_ERR_UNSUPPORTED"),

@@ -17,9 +17,9 @@ pytestmark = [pytest.mark.gpu,
 
 # (D, variant) pairs built into the library, besides the default kernel
 BUILT = [(64, 1), (64, 2), (64, 4), (64, 8), (64, 16), (64, 32), (64, 64), (64, 128),
-         (64, 256), (64, 512), (128, 2), (128, 16)]
+         (64, 256), (64, 512), (64, 1024), (64, 1152), (128, 2), (128, 16)]
 NAMES = {1: "ring3", 2: "exp_poly", 4: "wide", 8: "subpipe", 16: "sync", 32: "bar2",
-         64: "prod", 128: "trio", 256: "quad", 512: "rot"}
+         64: "prod", 128: "trio", 256: "quad", 512: "rot", 1024: "m32", 1152: "m32_trio"}
 
 SHAPES = [
     # B, H, S, causal, scale, seed
@@ -77,7 +77,7 @@ def test_variant_running_max_moves(D, variant):
         compare(o, l, O, L, f"lazy max D{D} {NAMES[variant]} causal={causal}")
 
 
-@pytest.mark.parametrize("variant", [1, 2, 4, 512], ids=lambda v: NAMES[v])
+@pytest.mark.parametrize("variant", [1, 2, 4, 512, 1024, 1152], ids=lambda v: NAMES[v])
 def test_variant_headline_full_compare(variant):
     w = WORKLOADS["sdpa_b1h8s4096d64"]
     q, k, v = workload_inputs(w)
