@@ -23,6 +23,7 @@ import numpy as np
 # Published MI355X dense peaks / bandwidth (no sparsity).
 PEAK_FP16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_SCLK_MHZ = 2400.0  # the shader clock the MFMA peak is quoted at
 # Exponential throughput used for the secondary (transcendental) bound: one
 # v_exp_f32 per visible score; a wave64 v_exp_f32 issues every 9 cycles per
 # SIMD (measured), 1024 SIMDs, at the 2.4 GHz peak clock.
@@ -52,6 +53,9 @@ def parse():
                          "variants and the key/value-cache (decode) timings")
     ap.add_argument("--sweep-steps", type=int, default=30,
                     help="timed launches per sweep point")
+    ap.add_argument("--clock-seconds", type=float, default=1.0,
+                    help="after the timed steps, run the step back to back this long while "
+                         "rocm-smi samples the shader clock (0: skip)")
     ap.add_argument("--cold", action="store_true",
                     help="also time launches with caches flushed (512 MB written before each)")
     ap.add_argument("--decode", default=None, metavar="WORKLOAD",
@@ -215,6 +219,61 @@ def prewarm(step, ms):
         n += 16
         torch.cuda.synchronize()
     return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "steps": n}
+
+
+SCLK_RE = re.compile(r"GPU\[(\d+)\].*sclk clock level: \d+: \((\d+)\s*Mhz\)", re.I)
+
+
+def parse_sclk(text: str):
+    """{gpu index: MHz} from `rocm-smi --showclocks` output."""
+    return {int(m.group(1)): int(m.group(2)) for m in SCLK_RE.finditer(text)}
+
+
+def sample_sclk(step, seconds: float):
+    """Run ``step`` back to back for ``seconds`` while a thread samples the
+    shader clock with rocm-smi (a child process). The MI355X holds its power
+    limit under this load, so the sustained clock, not the 2.4 GHz of the
+    peak figure, sets the ceiling of the achieved rate. None when rocm-smi
+    is missing or lists no single GPU."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+
+    exe = shutil.which("rocm-smi")
+    if exe is None or seconds <= 0:
+        return None
+    samples, gpus = [], set()
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=10)
+                clk = parse_sclk(r.stdout)
+                gpus.update(clk)
+                if len(clk) == 1:
+                    samples.append(next(iter(clk.values())))
+            except (OSError, subprocess.SubprocessError):
+                pass
+            stop.wait(0.05)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return None
+    # the first samples may still see the ramp; report the later half
+    late = samples[len(samples) // 2:]
+    return {"mhz_median": float(np.median(late)), "mhz_min": min(late), "mhz_max": max(late),
+            "samples": len(late), "seconds": seconds}
 
 
 def time_launches(step, stream, steps):
@@ -538,6 +597,9 @@ def main():
         f"{LAUNCH_GROUP}) avg {avg_ms * 1e3:.2f} us, median {np.median(durs_ms) * 1e3:.2f} us, "
         f"min {durs_ms.min() * 1e3:.2f} us")
 
+    sclk = sample_sclk(step, args.clock_seconds)
+    log(f"shader clock under sustained launches: {sclk}")
+
     ms_per_step = wall * 1e3 / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (avg_ms * 1e-3) / 1e12
@@ -568,6 +630,11 @@ def main():
                      "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4),
                      "traffic": traffic,
                      "kernel": kernel_label(w),
+                     # the shader clock sampled under the same launches, and the
+                     # fraction of the peak scaled to that clock (informative)
+                     "sclk_mhz": None if sclk is None else sclk["mhz_median"],
+                     "frac_at_sclk": (None if sclk is None else round(
+                         achieved / (PEAK_FP16_MFMA_TFLOPS * sclk["mhz_median"] / PEAK_SCLK_MHZ), 4)),
                      "algorithmic_flops_per_launch": w.flops,
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
         # secondary bounds at the same launch time: exponentials and HBM

@@ -105,3 +105,18 @@ def test_kernel_label_names_the_launched_instantiation():
     }
     for name, label in want.items():
         assert bench.kernel_label(WORKLOADS[name]) == label, name
+
+
+def test_parse_sclk_reads_each_gpu_clock():
+    """The rocm-smi clock lines the bench samples (one line per GPU; the
+    current level is the one reported)."""
+    text = ("============================ ROCm System Management Interface ============================\n"
+            "=================================== Current clock frequencies ===================================\n"
+            "GPU[0]\t\t: fclk clock level: 0: (1900Mhz)\n"
+            "GPU[0]\t\t: mclk clock level: 0: (1900Mhz)\n"
+            "GPU[0]\t\t: sclk clock level: 1: (2098Mhz)\n"
+            "GPU[0]\t\t: socclk clock level: 0: (28Mhz)\n")
+    assert bench.parse_sclk(text) == {0: 2098}
+    two = text + "GPU[1]\t\t: sclk clock level: 1: (1899Mhz)\n"
+    assert bench.parse_sclk(two) == {0: 2098, 1: 1899}
+    assert bench.parse_sclk("no clocks here") == {}
