@@ -135,3 +135,35 @@ def test_square_cache_is_the_self_attention_path_bitwise():
         outs.append((o.cpu().numpy().view(np.uint16), l.cpu().numpy().view(np.uint32)))
     for a, b in ((0, 1), (2, 3)):
         assert np.array_equal(outs[a][0], outs[b][0]) and np.array_equal(outs[a][1], outs[b][1])
+
+
+def _random_cases(n=20, seed=20261204):
+    """Random cache shapes: S_q from 1 to 400 queries against up to 6000
+    keys (S_q <= S_k under the causal mask, any S_q without it), both head
+    dimensions, random scales (negative and large ones), Q and K drawn
+    wider in some cases, and random or automatic run counts."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        Sk = int(rng.integers(1, 6000))
+        Sq = int(rng.integers(1, min(Sk, 400) + 1)) if causal else int(rng.integers(1, 401))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        mult = float(rng.choice([1.0, 1.0, 3.0]))
+        scale = (float(np.float32(1.0 / np.sqrt(D))) if rng.random() < 0.5
+                 else float(np.float32(rng.uniform(-1.5, 1.5))))
+        ns = "auto" if rng.random() < 0.4 else int(rng.integers(1, 33))
+        out.append((B, H, Sq, Sk, D, causal, scale, mult, ns, 9700 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: "B{}H{}q{}k{}D{}{}s{:.3f}x{}n{}".format(
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "n", c[6], c[7], c[8]))
+def test_kvcache_random_shape(case):
+    B, H, Sq, Sk, D, causal, scale, mult, ns, seed = case
+    print(f"[gpu-kvcache] random {case}", flush=True)
+    q, k, v = _cache_inputs(B, H, Sq, Sk, D, seed, qk_mult=mult)
+    o, l = _run(q, k, v, scale, causal, ns)
+    O, L = oracle_full(q, k, v, scale, causal, row_chunk=64)
+    compare(o, l, O, L, f"random kvcache {case}")
