@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--clock-seconds", type=float, default=1.0,
                     help="after the timed steps, run the step back to back this long while "
                          "rocm-smi samples the shader clock (0: skip)")
+    ap.add_argument("--gemm-seconds", type=float, default=1.0,
+                    help="time a plain fp16 library GEMM (8192^3, torch.matmul) back to back "
+                         "this long as a reference for the dense MFMA rate this box sustains "
+                         "(0: skip)")
     ap.add_argument("--cold", action="store_true",
                     help="also time launches with caches flushed (512 MB written before each)")
     ap.add_argument("--decode", default=None, metavar="WORKLOAD",
@@ -522,6 +526,38 @@ def run_decode(attn, dev, stream, steps, prewarm_ms, names=None):
     return out
 
 
+def gemm_reference(dev, seconds: float, n: int = 8192):
+    """Sustained rate of a plain fp16 GEMM from the vendor library
+    (torch.matmul -> hipBLASLt, fp32 accumulation) on this machine: a reference
+    for the dense MFMA rate a tuned contraction reaches at the power-limited
+    clock, beside the published peak. Not part of the attention path."""
+    import torch
+
+    if seconds <= 0:
+        return None
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(n, n, device=dev, generator=g).half()
+    b = torch.randn(n, n, device=dev, generator=g).half()
+    c = torch.empty(n, n, dtype=torch.float16, device=dev)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    rates = []
+    while time.perf_counter() - t0 < seconds:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(4):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        rates.append(4 * 2.0 * n ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    del a, b, c
+    late = rates[len(rates) // 2:]
+    return {"tflops": round(float(np.median(late)), 1), "m_n_k": [n, n, n], "dtype": "f16",
+            "library": "torch.matmul (hipBLASLt)", "seconds": seconds}
+
+
 def copy_calibration(dev):
     """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
     calibrate the HBM byte counters read for the attention kernels."""
@@ -599,6 +635,8 @@ def main():
 
     sclk = sample_sclk(step, args.clock_seconds)
     log(f"shader clock under sustained launches: {sclk}")
+    gemm = gemm_reference(dev, args.gemm_seconds)
+    log(f"fp16 library GEMM reference: {gemm}")
 
     ms_per_step = wall * 1e3 / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
@@ -633,6 +671,10 @@ def main():
                      # the shader clock sampled under the same launches, and the
                      # fraction of the peak scaled to that clock (informative)
                      "sclk_mhz": None if sclk is None else sclk["mhz_median"],
+                     # the rate a plain fp16 library GEMM sustains on the same box
+                     "gemm_reference_tflops": None if gemm is None else gemm["tflops"],
+                     "frac_of_gemm": (None if gemm is None
+                                      else round(achieved / gemm["tflops"], 4)),
                      "frac_at_sclk": (None if sclk is None else round(
                          achieved / (PEAK_FP16_MFMA_TFLOPS * sclk["mhz_median"] / PEAK_SCLK_MHZ), 4)),
                      "algorithmic_flops_per_launch": w.flops,
