@@ -180,8 +180,9 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *    scheduling of two consumer warpgroups, here with three).
  *  - ATTN_VARIANT_M32: both products on 32x32x16 MFMAs, each wave's 32
  *    query rows one MFMA block (the pages' kernels tile with the 5090's
- *    16x8x16 mma.sync atoms; Part 2, Move 4). Alone with two waves per
- *    SIMD, or with ATTN_VARIANT_TRIO (1152) with three.
+ *    m16n8k16 mma.sync atom: Part 2, the TILE setting of the Emmy knobs;
+ *    the Emmy comments, Hybrid FP16/FP32 Accumulation). Alone with two
+ *    waves per SIMD, or with ATTN_VARIANT_TRIO (1152) with three.
  *  - ATTN_VARIANT_SYNC: a check of the K/V ring protocol rather than an
  *    optimisation: every copy into LDS is waited for and followed by a
  *    workgroup barrier right after it is issued (and D = 128 runs lock-step,
