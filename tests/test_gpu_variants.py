@@ -28,6 +28,7 @@ SHAPES = [
     (1, 2, 640, True, -0.2, 3),
     (1, 1, 1000, False, 0.5, 4),
     (3, 2, 385, False, None, 5),
+    (2, 1, 1, True, 0.3, 6),          # one key: every tile masked past the first key
 ]
 
 
