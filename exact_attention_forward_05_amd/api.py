@@ -136,8 +136,9 @@ def choose_splits(B: int, H: int, S: int, D: int, causal: bool, n_cus: int = 256
                   Sk: Optional[int] = None) -> int:
     """Split count for attn_fwd_splitkv from a small cost model.
 
-    Each workgroup (one per CU: at D = 64 the registers of its eight waves,
-    two per SIMD, and at D = 128 its 160 KB of LDS leave room for no second)
+    Each workgroup (one per CU: the registers of its waves -- eight, two per
+    SIMD, or at D = 64 twelve, three per SIMD -- and at D = 128 its 136 KB of
+    LDS leave room for no second)
     costs its run of
     tile pairs plus a fixed cost per query tile it loads
     (:func:`_workgroup_costs`); workgroups are placed in launch order, largest
