@@ -15,12 +15,14 @@
 // take one tile each per interval (wave phase p folds tiles p, p + NPH, ...).
 // Wave w runs on SIMD w % 4, so the waves sharing a SIMD hold different query
 // rows and fill each other's stalls. Default: 8 waves, NPH = 2 tiles of 64
-// keys (two waves per SIMD); at D = 64 without the causal mask VAR_TRIO runs
-// 12 waves, NPH = 3 (three per SIMD). Other geometries are variants (see
-// Geometry). At the end the NPH carriers of a query group meet in LDS and each
-// wave merges them for the output columns it owns.
+// keys (two waves per SIMD); at D = 64 from 2048 keys (non-causal, and causal
+// single passes -- folded ones from 8192 keys) VAR_TRIO runs 12 waves,
+// NPH = 3 (three per SIMD). Other geometries are variants (see Geometry). At
+// the end the NPH carriers of a query group meet in LDS and each wave merges
+// them for the output columns it owns.
 //
-// MFMA: v_mfma_f32_16x16x32_f16. Lane l = 16*g + i (g = 0..3, i = 0..15):
+// MFMA: v_mfma_f32_16x16x32_f16 (the VAR_M32 variant: v_mfma_f32_32x32x16_f16,
+// its lane layout at Geometry::M32). Lane l = 16*g + i (g = 0..3, i = 0..15):
 //   A: row i, contraction slots (g, 0..7); B: column i, slots (g, 0..7);
 //   C: column i, rows 4*g + r (r = 0..3).
 // A slot (g, e) meets B slot (g, e), so any assignment of the contraction
