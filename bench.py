@@ -436,9 +436,12 @@ VARIANT_NAMES = {1: "ring3", 2: "exp_poly", 4: "wide", 8: "subpipe", 32: "bar2",
                  128: "trio", 256: "quad", 512: "rot", 1024: "m32", 1152: "m32_trio"}
 
 
-def run_variants(attn, dev, stream, steps, prewarm_ms):
+def run_variants(attn, dev, stream, steps, prewarm_ms, rounds: int = 3):
     """Kernel time of each compiled variant against the default kernel on the
-    same inputs, default first, each pre-warmed (attn_fwd_variant)."""
+    same inputs (attn_fwd_variant): ``rounds`` rounds, each timing the default
+    and then every variant, each pre-warmed; medians over the rounds, so that
+    a drift of the power-limited clock during the section does not favour
+    whichever build runs in a given place of the order."""
     import torch
 
     from testkit import WORKLOADS, workload_inputs
@@ -460,15 +463,24 @@ def run_variants(attn, dev, stream, steps, prewarm_ms):
             durs, _ = time_launches(fn, stream, steps)
             return float(durs.mean()) * 1e3
 
+        # every build once through the checked binding, then raw launches
         attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
-        base_us = timed(raw_step("attn_fwd", q, k, v, o, lse, w, stream))
         for var in variants:
             attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream,
                      variant=var)
-            us = timed(raw_step("attn_fwd_variant", q, k, v, o, lse, w, stream, extra=(var,)))
+        steps_of = {0: raw_step("attn_fwd", q, k, v, o, lse, w, stream)}
+        for var in variants:
+            steps_of[var] = raw_step("attn_fwd_variant", q, k, v, o, lse, w, stream, extra=(var,))
+        times = {key: [] for key in steps_of}
+        for _ in range(rounds):
+            for key, fn in steps_of.items():
+                times[key].append(timed(fn))
+        base_us = float(np.median(times[0]))
+        for var in variants:
+            us = float(np.median(times[var]))
             rec = {"workload": name, "variant": VARIANT_NAMES[var], "default_us": round(base_us, 3),
                    "variant_us": round(us, 3), "variant_tflops": round(w.flops / (us * 1e-6) / 1e12, 2),
-                   "ratio": round(us / base_us, 4)}
+                   "ratio": round(us / base_us, 4), "rounds": rounds}
             log(f"variant {rec}")
             out.append(rec)
         del q, k, v, o, lse
