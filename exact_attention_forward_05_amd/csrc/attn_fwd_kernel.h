@@ -79,9 +79,14 @@ constexpr int INTERVAL_KEYS = 128;    // keys per barrier interval
 constexpr int COMBINE_THREADS = 256;  // combine kernel: four waves, one row each
 constexpr int MAX_SPLITS = 64;        // key runs per query tile of a split launch, at most
 constexpr float NEG_BIG = -1.0e30f;   // finite stand-in for -infinity
-// Lazy-max bound on a lane's tile sum: every probability stays below it, and
-// so below fp16's largest finite value (65504) with room for rounding.
-constexpr float P_LIMIT = 32768.0f;
+// Lazy-max bound on a lane's tile sum. The sum is taken over the fp16-rounded
+// probabilities, so every rounded probability is at most the sum, and a value
+// that overflowed to infinity fails the test. 65504 (fp16's largest finite
+// value) less a margin of 4064 for the fp32 rounding of the running sum
+// against d (d stays below about 2^30 even for a 2^20-key row under this
+// bound, where that rounding is a few hundred at most). Against 2^15: 2.5%
+// faster on peaked D = 64 rows (Q and K x 3), the same elsewhere.
+constexpr float P_LIMIT = 61440.0f;
 // A redo sets the running max to the tile's max itself. (Setting it some
 // margin h above, so that a row whose max keeps climbing redoes less often,
 // shifts every later probability of the row down by 2^-h: with h = 8 those
