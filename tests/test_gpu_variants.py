@@ -88,6 +88,22 @@ def test_variant_headline_full_compare(variant):
           f"{compare(o, l, O, L, f'headline {NAMES[variant]}')}", flush=True)
 
 
+@pytest.mark.parametrize("variant", [1024, 1152], ids=lambda v: NAMES[v])
+@pytest.mark.parametrize("causal,scale,mult", [(True, 0.125, 1.0), (True, -0.3, 3.0),
+                                               (False, 1.0, 1.0)],
+                         ids=["causal", "causal_peaked_negative", "noncausal_scale1"])
+def test_m32_long_rows(variant, causal, scale, mult):
+    """32x32x16 MFMAs over 2500 keys (a ragged tail in the three-wave
+    geometry's 192-key intervals), with the causal diagonal, peaked and
+    negative-scale scores."""
+    print(f"[gpu-variants] {NAMES[variant]} S2500 causal={causal} scale={scale} x{mult}",
+          flush=True)
+    q, k, v = make_qkv(1, 2, 2500, 64, 9650 + variant % 7, qk_mult=mult)
+    o, l = run_variant(q, k, v, scale, causal, variant)
+    O, L = oracle.sdpa_forward(q, k, v, scale, causal)
+    compare(o, l, O, L, f"{NAMES[variant]} S2500 causal={causal} scale={scale}")
+
+
 def test_exp_poly_peaked_causal_d128():
     """The exponential offload at D = 128 on a slice of the peaked causal
     workload (Q, K x 3): 8 heads of S = 4096, every row compared."""
