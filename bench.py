@@ -406,15 +406,23 @@ def run_splitkv(attn, dev, stream, steps, prewarm_ms):
         split = raw_step("attn_fwd_splitkv", q, k, v, o, lse, w, stream,
                          extra=(ns, ws.data_ptr(), ws.numel()))
 
-        rec = {"workload": name, "n_splits": ns}
-        for tag, fn in (("single_pass", single), ("splitkv", split)):
-            prewarm(fn, prewarm_ms)
-            for _ in range(5):
-                fn()
-            durs, _ = time_launches(fn, stream, steps)
-            rec[f"{tag}_us_mean"] = round(float(durs.mean()) * 1e3, 3)
-            rec[f"{tag}_us_median"] = round(float(np.median(durs)) * 1e3, 3)
-            rec[f"{tag}_tflops"] = round(w.flops / (float(durs.mean()) * 1e-3) / 1e12, 2)
+        # three interleaved rounds (as for the variants): per tag, the round
+        # means and medians, reported as their medians
+        rec = {"workload": name, "n_splits": ns, "rounds": 3}
+        runs = {"single_pass": ([], []), "splitkv": ([], [])}
+        for _ in range(3):
+            for tag, fn in (("single_pass", single), ("splitkv", split)):
+                prewarm(fn, prewarm_ms)
+                for _ in range(5):
+                    fn()
+                durs, _ = time_launches(fn, stream, steps)
+                runs[tag][0].append(float(durs.mean()) * 1e3)
+                runs[tag][1].append(float(np.median(durs)) * 1e3)
+        for tag, (means, medians) in runs.items():
+            mean_us = float(np.median(means))
+            rec[f"{tag}_us_mean"] = round(mean_us, 3)
+            rec[f"{tag}_us_median"] = round(float(np.median(medians)), 3)
+            rec[f"{tag}_tflops"] = round(w.flops / (mean_us * 1e-6) / 1e12, 2)
         rec["speedup"] = round(rec["single_pass_us_mean"] / rec["splitkv_us_mean"], 3)
         log(f"splitkv {name}: {rec}")
         out.append(rec)
