@@ -86,3 +86,52 @@ def _long_cases(n=8, seed=20261203):
     c[0], c[1], c[2], c[3], "c" if c[4] else "n", c[5], c[6], c[7]))
 def test_random_long_shape(case):
     test_random_shape(case)
+
+
+def _extreme_cases(n=40, seed=20261205):
+    """Random shapes with scales up to 6 in magnitude and Q, K up to 3x wider:
+    scores spanning hundreds of log2 units, so a row's probabilities are one
+    key's or a few keys' (the lazy max redoes often, most probabilities
+    vanish). A third of the cases run as S_q < S_k caches."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        Sk = int(rng.integers(1, 2600))
+        cache = rng.random() < 0.33
+        if cache:
+            Sq = int(rng.integers(1, min(Sk, 300) + 1)) if causal else int(rng.integers(1, 300))
+        else:
+            Sq = Sk
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        mult = float(rng.choice([1.0, 2.0, 3.0]))
+        scale = float(np.float32(rng.uniform(-6.0, 6.0)))
+        n_splits = int(rng.integers(1, 17))
+        out.append((B, H, Sq, Sk, D, causal, scale, mult, n_splits, 5000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _extreme_cases(), ids=lambda c: "B{}H{}q{}k{}D{}{}s{:.2f}x{}n{}".format(
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "n", c[6], c[7], c[8]))
+def test_random_extreme_scales(case):
+    import torch
+
+    import exact_attention_forward_05_amd as attn
+
+    B, H, Sq, Sk, D, causal, scale, mult, n_splits, seed = case
+    print(f"[gpu-random] extreme {case}", flush=True)
+    q, _, _ = make_qkv(B, H, Sq, D, seed, qk_mult=mult)
+    _, k, v = make_qkv(B, H, Sk, D, seed + 7919, qk_mult=mult)
+    O, L = oracle.sdpa_forward(q, k, v, scale, causal)
+    dev = torch.device("cuda:0")
+    qt, kt, vt = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    runs = [("kvcache", attn.fwd_kvcache(qt, kt, vt, n_splits=n_splits, scale=scale,
+                                         causal=causal))]
+    if Sq == Sk:
+        runs.append(("single pass", attn.fwd(qt, kt, vt, scale=scale, causal=causal)))
+        runs.append(("split-KV", attn.fwd_splitkv(qt, kt, vt, n_splits=n_splits, scale=scale,
+                                                  causal=causal)))
+    torch.cuda.synchronize()
+    for tag, (o, l) in runs:
+        compare(o.cpu().numpy(), l.cpu().numpy(), O, L, f"{tag} {case}")
