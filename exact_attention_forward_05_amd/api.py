@@ -65,6 +65,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float
     ``out``/``lse`` may be preallocated. The call is asynchronous on ``stream``
     (default: torch's current stream). ``variant`` selects a compiled kernel
     variant (``_lib.VARIANT_*``; 0 is the default kernel).
+
+    One workgroup folds each 128-row query tile, so a problem with fewer
+    tiles than the GPU has CUs (B*H*ceil(S/128) < 256 on MI355X), or a causal
+    one whose longest tiles dominate, leaves CUs idle: :func:`fwd_splitkv`
+    with ``n_splits="auto"`` spreads the keys over more workgroups there.
     """
     B, H, S, D, scale, out, lse, stream = _prepare(q, k, v, scale, out, lse, stream)
     with torch.cuda.device(q.device):
